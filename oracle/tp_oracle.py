@@ -1,0 +1,249 @@
+"""Float64 oracle of the tensor-parallel FFN and attention sublayer shards.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain definitions,
+written out step by step; numpy.matmul serves as the matrix product.
+
+Conventions (the row-vector form used by the code on "Tensor & Pipeline
+Parallelism" (llminference, S17), section "Core idea": ``x @ w1``):
+    X [T, d], W1/W3 [d, d_ff], W2 [d_ff, d], Wq [d, n_heads*d_h],
+    Wk/Wv [d, n_kv_heads*d_h], Wo [n_heads*d_h, d]; everything row-major.
+The column-vector form of "7.9 Tensor and pipeline parallelism" section 2.1
+(y = W2 sigma(W1 x), W1 in R^{d_ff x d}) is the transpose of this and shards
+the same d_ff hidden units.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy import special as _sp
+
+ACTS = ("none", "gelu", "swiglu", "bilinear")
+
+
+# ----------------------------------------------------------------------------- shards
+def shard_range(extent: int, T_p: int, t: int) -> tuple[int, int]:
+    """Block of ``extent`` owned by rank t of T_p: (begin, length).
+
+    "7.9 Tensor and pipeline parallelism" section 2.1: the d_ff hidden units
+    are divided into T_p groups and device t holds group t.  An extent that
+    T_p does not divide is an error (the pages only divide evenly).
+    """
+    if T_p < 1 or not (0 <= t < T_p):
+        raise ValueError(f"rank {t} out of range for T_p={T_p}")
+    if extent < 0:
+        raise ValueError("negative extent")
+    if extent % T_p:
+        raise ValueError(f"extent {extent} not divisible by T_p={T_p}")
+    n = extent // T_p
+    return t * n, n
+
+
+def head_shard(n_heads: int, n_kv_heads: int, head_dim: int, T_p: int, t: int) -> dict:
+    """Heads owned by rank t, and the column (Wq/Wk/Wv) / row (Wo) blocks they index.
+
+    "7.9 Tensor and pipeline parallelism" section 2.2 (device t owns h/T_p
+    heads) and the ShardedAttention listing on "Tensor & Pipeline
+    Parallelism" (llminference, S17), section "Implementation": T_p must
+    divide both the query-head and the KV-head counts.
+    """
+    if n_heads % T_p:
+        raise ValueError(f"TP degree {T_p} must divide query heads ({n_heads})")
+    if n_kv_heads % T_p:
+        raise ValueError(f"TP{T_p} needs n_kv_heads divisible by {T_p}, got {n_kv_heads}")
+    h_t = n_heads // T_p
+    kv_t = n_kv_heads // T_p
+    return {
+        "h_t": h_t,
+        "kv_t": kv_t,
+        "q_cols": (t * h_t * head_dim, (t + 1) * h_t * head_dim),
+        "kv_cols": (t * kv_t * head_dim, (t + 1) * kv_t * head_dim),
+        "o_rows": (t * h_t * head_dim, (t + 1) * h_t * head_dim),
+    }
+
+
+# ----------------------------------------------------------------------------- activations
+def gelu(u: np.ndarray) -> np.ndarray:
+    """GELU, erf form: u * Phi(u) = u/2 * (1 + erf(u / sqrt 2)) = u/2 * erfc(-u / sqrt 2).
+
+    The pages name GeLU/GELU without a formula ("Tensor and Pipeline
+    Parallelism" lesson on grasp.study, "A Tale of Two GEMMs"; "Parallelism II:
+    model", "Tensor parallelism"); the exact (erf) form is taken.  It is
+    evaluated through erfc so that the far negative tail keeps its relative
+    accuracy (1 + erf cancels there).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * u * _sp.erfc(-u / math.sqrt(2.0))
+
+
+def silu(u: np.ndarray) -> np.ndarray:
+    """silu(u) = u / (1 + exp(-u)), as used by the ShardedFFN listing (S17, "Core idea")."""
+    u = np.asarray(u, dtype=np.float64)
+    return u / (1.0 + np.exp(-u))
+
+
+# ----------------------------------------------------------------------------- FFN
+def column_parallel(x, w1, w3, cols: tuple[int, int], act: str) -> np.ndarray:
+    """H(t) = sigma(X . W1[:, cols]) -- or silu(X.W1[:,cols]) * (X.W3[:,cols]).
+
+    "7.9 ..." section 2.1 eq. for h^(t): x is the same on every device and
+    the element-wise non-linearity is applied to the rank's hidden slice with
+    no communication.  S17 "Core idea": h = silu(x @ w1) * (x @ w3) with W1
+    and W3 split on their output dimension.  "bilinear" is the gate with no
+    non-linearity, U * V; "none" returns U (both used for exact tests).
+    """
+    if act not in ACTS:
+        raise ValueError(act)
+    b, e = cols
+    x = np.asarray(x, dtype=np.float64)
+    u = x @ np.asarray(w1[:, b:e], dtype=np.float64)
+    if act == "none":
+        return u
+    if act == "gelu":
+        return gelu(u)
+    v = x @ np.asarray(w3[:, b:e], dtype=np.float64)
+    if act == "swiglu":
+        return silu(u) * v
+    return u * v
+
+
+def row_parallel(h, w2, rows: tuple[int, int]) -> np.ndarray:
+    """y(t) = H(t) . W2[rows, :] -- the rank's partial sum of the output.
+
+    "7.9 ..." section 2.1 eq. for y^(t) (row shard of W2 over the same
+    groups); S17 "Core idea": y = h @ w2 is a PARTIAL sum.
+    """
+    b, e = rows
+    return np.asarray(h, dtype=np.float64) @ np.asarray(w2[b:e, :], dtype=np.float64)
+
+
+def ffn_shard(x, w1, w3, w2, T_p: int, t: int, act: str):
+    """Rank t's FFN share: returns (H(t), y(t))."""
+    d_ff = w1.shape[1]
+    b, n = shard_range(d_ff, T_p, t)
+    h = column_parallel(x, w1, w3, (b, b + n), act)
+    return h, row_parallel(h, w2, (b, b + n))
+
+
+def ffn_unsharded(x, w1, w3, w2, act: str) -> np.ndarray:
+    """The full sublayer y = sigma(X W1) W2 (or (silu(XW1) * XW3) W2), no sharding."""
+    h = column_parallel(x, w1, w3, (0, w1.shape[1]), act)
+    return row_parallel(h, w2, (0, w2.shape[0]))
+
+
+def partial_sum(parts, residual=None) -> np.ndarray:
+    """y = sum_t y(t) [+ residual] -- what the all-reduce g computes.
+
+    "7.9 ..." section 2.1: the full output is the sum over devices of the
+    partial sums; one all-reduce at the end of the FFN gives every device y.
+    Summed in ascending t; the residual (used by the block) is added last.
+    """
+    acc = np.zeros_like(np.asarray(parts[0], dtype=np.float64))
+    for p in parts:
+        acc = acc + np.asarray(p, dtype=np.float64)
+    if residual is not None:
+        acc = acc + np.asarray(residual, dtype=np.float64)
+    return acc
+
+
+# ----------------------------------------------------------------------------- attention
+def attn_outproj_shard(o_t, wo, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
+                       t: int) -> np.ndarray:
+    """a(t) = O(t) . Wo[rows(t), :] -- row-sharded output projection.
+
+    "7.9 ..." section 2.2 eq. attn-out^(t) = W_O^(t) head-output^(t), then an
+    all-reduce; S17 "Implementation": ``self.wo = w.wo[h, :]`` (row shard by
+    the rank's heads).
+    """
+    hs = head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
+    b, e = hs["o_rows"]
+    o_t = np.asarray(o_t, dtype=np.float64)
+    if o_t.shape[1] != e - b:
+        raise ValueError("O(t) width must be h_t * head_dim")
+    return o_t @ np.asarray(wo[b:e, :], dtype=np.float64)
+
+
+def attention_head(q, k, v, causal: bool = True, rows=None) -> np.ndarray:
+    """softmax(Q K^T / sqrt(d_h) [+ causal mask]) V for one head.
+
+    Scaled dot-product attention, computed per head with no communication
+    ("7.9 ..." section 2.2: Q, K, V projections, softmax and value mixing are
+    local to the device owning the head).  Causal: query i sees keys k <= i.
+    ``rows`` restricts the computed query rows (q is then the full Q, and only
+    those rows are returned).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, dh = q.shape
+    idx = np.arange(T) if rows is None else np.asarray(rows)
+    s = (q[idx] @ k.T) / math.sqrt(dh)
+    if causal:
+        mask = np.arange(k.shape[0])[None, :] > idx[:, None]
+        s = np.where(mask, -np.inf, s)
+    s = s - np.max(s, axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / np.sum(p, axis=1, keepdims=True)
+    return p @ v
+
+
+def attn_heads_shard(x, wq, wk, wv, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
+                     t: int, causal: bool = True, rows=None) -> np.ndarray:
+    """O(t): the rank's heads' outputs concatenated, [T (or len(rows)), h_t*head_dim].
+
+    Column shards of Wq (and of Wk/Wv by KV head) by head, per S17
+    "Implementation" (``w.wq[:, h]``, KV sharded by KV head); local query head
+    j of rank t reads KV head j // (h_t / kv_t) of that rank (grouped-query
+    attention; with n_kv_heads == n_heads this is ordinary multi-head
+    attention).
+    """
+    hs = head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
+    x = np.asarray(x, dtype=np.float64)
+    qb, _ = hs["q_cols"]
+    kb, _ = hs["kv_cols"]
+    group = hs["h_t"] // hs["kv_t"]
+    outs = []
+    need = x if rows is None else x[: int(np.max(rows)) + 1]
+    for j in range(hs["h_t"]):
+        c0 = qb + j * head_dim
+        kc = kb + (j // group) * head_dim
+        q = need @ np.asarray(wq[:, c0:c0 + head_dim], dtype=np.float64)
+        k = need @ np.asarray(wk[:, kc:kc + head_dim], dtype=np.float64)
+        v = need @ np.asarray(wv[:, kc:kc + head_dim], dtype=np.float64)
+        outs.append(attention_head(q, k, v, causal=causal, rows=rows))
+    return np.concatenate(outs, axis=1)
+
+
+def block_sequence(x_s, w, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
+                   act: str = "gelu", rows=None):
+    """One sequence through a TP block shard set, all T_p ranks: returns (x1, y).
+
+    Attention sublayer (heads sharded, row-sharded Wo) -> sum over ranks
+    (g) + residual -> FFN sublayer (column/row sharded) -> sum over ranks (g)
+    + residual.  "7.9 ..." section 2.2: two all-reduces per block; LayerNorm,
+    dropout and biases are outside the sharded matmuls and are not part of
+    this computation.  ``w`` holds full wq, wk, wv, wo, w1, w3 (or None), w2.
+    With ``rows`` only those token rows of x1 and y are returned.
+    """
+    x_s = np.asarray(x_s, dtype=np.float64)
+    a_parts = []
+    for t in range(T_p):
+        o_t = attn_heads_shard(x_s, w["wq"], w["wk"], w["wv"], n_heads, n_kv_heads, head_dim,
+                               T_p, t, causal=True, rows=rows)
+        a_parts.append(attn_outproj_shard(o_t, w["wo"], n_heads, n_kv_heads, head_dim, T_p, t))
+    res = x_s if rows is None else x_s[np.asarray(rows)]
+    x1 = partial_sum(a_parts, residual=res)
+    y_parts = [ffn_shard(x1, w["w1"], w.get("w3"), w["w2"], T_p, t, act)[1] for t in range(T_p)]
+    return x1, partial_sum(y_parts, residual=x1)
+
+
+# ----------------------------------------------------------------------------- comparison
+def normwise_max_rel_err(got, ref) -> float:
+    """max|G - R| / max|R| (0 when both are all zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den

@@ -1,0 +1,96 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case replaces one oracle function by a plausible wrong version (on the
+CPU only) and checks that at least one pin test then fails.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import test_oracle_pins as pins
+from oracle import tp_oracle as O
+
+
+def _wrong_silu_sign(u):
+    u = np.asarray(u, dtype=np.float64)
+    return u / (1.0 + np.exp(u))
+
+
+def _tanh_gelu(u):
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * u * (1 + np.tanh(math.sqrt(2 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+def _reversed_ranks(extent, T_p, t):
+    n = extent // T_p
+    if extent % T_p or not (0 <= t < T_p):
+        raise ValueError
+    return (T_p - 1 - t) * n, n
+
+
+def _drop_last_partial(parts, residual=None):
+    acc = np.zeros_like(np.asarray(parts[0], dtype=np.float64))
+    for p in parts[:-1] if len(parts) > 1 else parts:
+        acc = acc + p
+    return acc if residual is None else acc + residual
+
+
+_orig_attention = O.attention_head
+
+
+def _unscaled_attention(q, k, v, causal=True, rows=None):
+    """Drops the 1/sqrt(d_h) scale (pre-multiplying Q by sqrt(d_h) cancels it)."""
+    q = np.asarray(q, dtype=np.float64)
+    return _orig_attention(q * math.sqrt(q.shape[1]), k, v, causal, rows)
+
+
+def _mask_diagonal_too(q, k, v, causal=True, rows=None):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, dh = q.shape
+    idx = np.arange(T) if rows is None else np.asarray(rows)
+    s = (q[idx] @ k.T) / math.sqrt(dh)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] >= idx[:, None], -1e300, s)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def _transposed_w2(h, w2, rows):
+    b, e = rows
+    w = np.asarray(w2, dtype=np.float64)
+    blk = w[b:e, :]
+    if blk.shape[0] == blk.shape[1]:
+        blk = blk.T
+    else:
+        blk = blk[::-1]
+    return np.asarray(h, dtype=np.float64) @ blk
+
+
+MUTATIONS = [
+    ("silu", _wrong_silu_sign, [lambda: pins.test_silu_closed_forms_and_library(),
+                                lambda: pins.test_brute_force_tiny("swiglu", 2)]),
+    ("gelu", _tanh_gelu, [lambda: pins.test_gelu_closed_forms_and_library(),
+                          lambda: pins.test_brute_force_tiny("gelu", 1)]),
+    ("shard_range", _reversed_ranks, [lambda: pins.test_brute_force_tiny("gelu", 2),
+                                      lambda: pins.test_shard_range_blocks()]),
+    ("partial_sum", _drop_last_partial, [lambda: pins.test_sum_of_partials_is_unsharded_ffn_tp1_to_tp11("gelu")]),
+    ("attention_head", _unscaled_attention, [lambda: pins.test_attention_vs_library_sdpa(True)]),
+    ("attention_head", _mask_diagonal_too, [lambda: pins.test_attention_special_cases(),
+                                            lambda: pins.test_attention_brute_force()]),
+    ("row_parallel", _transposed_w2, [lambda: pins.test_brute_force_tiny("none", 2)]),
+]
+
+
+@pytest.mark.parametrize("name,wrong,checks", MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, wrong, checks):
+    monkeypatch.setattr(O, name, wrong)
+    for check in checks:
+        with pytest.raises((AssertionError, ValueError)):
+            check()
