@@ -1,0 +1,188 @@
+/*
+ * tpshard.h -- C ABI of one tensor-parallel rank's share of a Megatron-style
+ * transformer sublayer, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (row-vector convention, everything row-major):
+ *
+ *   FFN sublayer, rank t of T_p ("7.9 Tensor and pipeline parallelism",
+ *   section 2.1, the column-shard of W1 and row-shard of W2; the ShardedFFN
+ *   listing of "Tensor & Pipeline Parallelism" (llminference S17),
+ *   section "Core idea"):
+ *       n      = d_ff / T_p,  cols(t) = [t*n, (t+1)*n)
+ *       H(t)   = act(X . W1[:, cols(t)])                      (GELU, erf form)
+ *              | silu(X . W1[:, cols(t)]) * (X . W3[:, cols(t)])   (SwiGLU)
+ *       y(t)   = H(t) . W2[cols(t), :]        -- the rank's partial sum
+ *   Attention output projection, rank t (same page, section 2.2;
+ *   S17 "Implementation", the row shard of wo by the rank's heads):
+ *       a(t)   = O(t) . Wo[rows(t), :],  rows(t) = [t*h_t*d_h, (t+1)*h_t*d_h)
+ *   Head-sharded attention core (section 2.2: projections, softmax and value
+ *   mixing of the rank's heads are local):
+ *       O(t)   = [softmax(Q_j K_j^T / sqrt(d_h) + causal mask) V_j]_j
+ *   All-reduce "g" (section 2.1: y = sum over ranks of y(t)), here the local
+ *   stand-in that adds all T_p partials held on one GPU:
+ *       y      = sum_{t=0}^{T_p-1} y(t)  [+ residual]
+ *
+ * Conventions shared by every entry point:
+ *  - Weights are passed UNSHARDED (the full W1/W3 [d, d_ff], W2 [d_ff, d],
+ *    Wq [d, n_heads*d_h], Wk/Wv [d, n_kv_heads*d_h], Wo [n_heads*d_h, d]);
+ *    the library applies the rank's offsets.  A caller holding only its own
+ *    shard passes the shard's extent with T_p = 1, t = 0.
+ *  - All pointers are DEVICE pointers owned by the caller, 16-byte aligned.
+ *    The library never allocates, frees or synchronises: it enqueues kernels
+ *    on `hip_stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Every argument check runs on the host before any launch.  A non-zero
+ *    status leaves all outputs untouched; tp_last_error() then describes it.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Shapes that T_p does not divide are errors (TP_ERR_NOT_DIVISIBLE), as
+ *    the pages only ever divide evenly.
+ *  - Row (token) counts may be anything >= 0 (0 is a no-op).  Feature
+ *    extents (d, n, h_t*d_h) must be multiples of 8 (bf16) or 4 (fp32) so
+ *    every row is made of whole 16-byte vectors (TP_ERR_UNSUPPORTED).
+ *  - Arithmetic: bf16 inputs are multiplied on MFMA with fp32 accumulation;
+ *    the activation runs on the fp32 accumulator and H(t) is rounded once to
+ *    bf16 (round-to-nearest-even).  fp32 inputs stay fp32 throughout.
+ *  - Thread safety: calls may be issued from several host threads; the
+ *    error message is thread-local.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPSHARD_ABI_VERSION 1
+
+/* Status codes. */
+#define TP_OK                 0
+#define TP_ERR_INVALID_ARG   -1  /* null/misaligned pointer, negative or out-of-range size, rank >= T_p */
+#define TP_ERR_NOT_DIVISIBLE -2  /* d_ff, n_heads or n_kv_heads not divisible by T_p */
+#define TP_ERR_WORKSPACE     -3  /* workspace missing or smaller than the query says */
+#define TP_ERR_UNSUPPORTED   -4  /* dtype / activation combination or extent not supported */
+#define TP_ERR_HIP           -5  /* a HIP runtime call or kernel launch failed */
+
+/* Activation of the column-parallel GEMM's epilogue. */
+#define TP_ACT_NONE      0  /* H = U (no activation)                                */
+#define TP_ACT_GELU      1  /* H = U * Phi(U) = U/2 (1 + erf(U / sqrt 2))           */
+#define TP_ACT_SWIGLU    2  /* H = silu(U) * V,  U = X.W1(t), V = X.W3(t)           */
+#define TP_ACT_BILINEAR  3  /* H = U * V (gate with no non-linearity)               */
+
+/* Element types. */
+#define TP_F32   0
+#define TP_BF16  1
+
+/* ABI version of the loaded library (TPSHARD_ABI_VERSION). */
+int tp_abi_version(void);
+
+/* Message of the calling thread's last non-zero status ("" if none). The
+ * pointer stays valid until the thread's next call into the library. */
+const char* tp_last_error(void);
+
+/*
+ * Block of `extent` owned by rank t of T_p: *begin = t*(extent/T_p),
+ * *len = extent/T_p ("7.9 Tensor and pipeline parallelism", section 2.1:
+ * the d_ff hidden units are divided into T_p groups, device t holds group
+ * t).  Host-only integer arithmetic.  Errors: TP_ERR_INVALID_ARG (T_p < 1,
+ * t outside [0, T_p), extent < 0, null outputs), TP_ERR_NOT_DIVISIBLE.
+ */
+int tp_shard_range(int64_t extent, int32_t T_p, int32_t t, int64_t* begin, int64_t* len);
+
+/*
+ * Bytes of device workspace tp_ffn_shard_fwd needs to hold H(t):
+ * T * (d_ff/T_p) * sizeof(element of in_dtype), rounded up to 256 bytes.
+ * Returns 0 for invalid arguments (and for T == 0).
+ */
+size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_dtype);
+
+/*
+ * FFN share of rank t: y_t = act(x . W1(t) [, x . W3(t)]) . W2(t).
+ *
+ *   x         [T, d]      in_dtype
+ *   w1, w3    [d, d_ff]   in_dtype, full matrices (w3 only for SWIGLU/BILINEAR,
+ *                         must be NULL otherwise)
+ *   w2        [d_ff, d]   in_dtype, full matrix
+ *   y_t       [T, d]      out_dtype: the rank's partial sum (written, not accumulated)
+ *   workspace             >= tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype); receives
+ *                         H(t) [T, d_ff/T_p] in in_dtype (readable by the caller after
+ *                         the stream reaches this point)
+ *   in_dtype / out_dtype  (BF16, BF16), (BF16, F32) or (F32, F32)
+ *
+ * Two kernels are enqueued: the column-parallel GEMM with the activation
+ * fused into its epilogue, then the row-parallel GEMM.  No communication.
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_NOT_DIVISIBLE (d_ff % T_p),
+ * TP_ERR_WORKSPACE, TP_ERR_UNSUPPORTED, TP_ERR_HIP.
+ */
+int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* w2,
+                     void* y_t, void* workspace, size_t workspace_bytes,
+                     int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
+                     int32_t act, int32_t in_dtype, int32_t out_dtype, void* hip_stream);
+
+/*
+ * Row-sharded attention output projection of rank t: y_t = o_t . Wo[rows(t), :].
+ *
+ *   o_t   [T, h_t*head_dim]         in_dtype, the rank's heads' outputs, contiguous
+ *   wo    [n_heads*head_dim, d]     in_dtype, full matrix
+ *   y_t   [T, d]                    out_dtype, the rank's partial sum
+ * h_t = n_heads / T_p.  Both n_heads and n_kv_heads must be divisible by T_p
+ * (the GQA constraint of S17, "Attention shards by head, and GQA caps the
+ * degree"): otherwise TP_ERR_NOT_DIVISIBLE and nothing is launched.
+ */
+int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t,
+                              int64_t T, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t T_p, int32_t t,
+                              int32_t in_dtype, int32_t out_dtype, void* hip_stream);
+
+/*
+ * Bytes of device workspace tp_attn_heads_shard_fwd needs (the rank's Q, K
+ * and V): n_seq*seq_len * (h_t + 2*kv_t) * head_dim * 2, rounded up to 256.
+ * Returns 0 for invalid arguments.
+ */
+size_t tp_attn_heads_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t T_p);
+
+/*
+ * Head-sharded attention of rank t (bf16 only): for each of the rank's h_t
+ * query heads j (global head t*h_t + j) and its KV head (grouped-query: local
+ * KV head j / (h_t/kv_t)):
+ *     Q_j = x . Wq[:, head cols],  K_j = x . Wk[:, kv cols],  V_j = x . Wv[:, kv cols]
+ *     O_j = softmax(Q_j K_j^T / sqrt(head_dim) [+ causal mask: key <= query]) V_j
+ * independently for each of the n_seq sequences of seq_len tokens in x.
+ *
+ *   x          [n_seq*seq_len, d]            bf16
+ *   wq         [d, n_heads*head_dim]         bf16, full
+ *   wk, wv     [d, n_kv_heads*head_dim]      bf16, full
+ *   o_t        [n_seq*seq_len, h_t*head_dim] bf16, head j in columns [j*head_dim, (j+1)*head_dim)
+ *   workspace  >= tp_attn_heads_workspace_bytes(...)
+ * head_dim must be 64 or 128.  causal: 1 = causal mask, 0 = none.
+ */
+int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                            void* o_t, void* workspace, size_t workspace_bytes,
+                            int64_t n_seq, int64_t seq_len, int64_t d,
+                            int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int32_t T_p, int32_t t, int32_t causal, void* hip_stream);
+
+/*
+ * Local partial sum standing in for the all-reduce ("7.9 Tensor and
+ * pipeline parallelism", section 2.1: y is the sum over ranks of y(t)):
+ *     y[i] = sum_{t=0}^{T_p-1} partials[t*partial_stride + i]  (+ residual[i])
+ * accumulated in fp32 in ascending t, residual added last, rounded once to
+ * out_dtype.  The order is fixed, so repeated calls are bitwise identical.
+ *
+ *   partials        T_p slices of n_elems elements, part_dtype, slice t at
+ *                   offset t*partial_stride elements (partial_stride >= n_elems)
+ *   residual        NULL or [n_elems] out_dtype; may equal y (in place)
+ *   y               [n_elems] out_dtype; must not overlap the partials
+ * Supported: part_dtype and out_dtype each BF16 or F32.  n_elems == 0 is a no-op.
+ */
+int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p,
+                   const void* residual, void* y, int64_t n_elems,
+                   int32_t part_dtype, int32_t out_dtype, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -1,0 +1,249 @@
+// C ABI of the tensor-parallel shard library (declarations and contract in tpshard.h).
+//
+// Host side only: argument validation (everything is checked before any launch),
+// the rank's offsets into the full weight matrices, kernel selection, and
+// error reporting.  Kernels live in gemm_bf16.hip, gemm_f32.hip, partial_sum.hip
+// and attention.hip.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "tp_internal.h"
+#include "tpshard.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TP_OK;
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Largest leading dimension / feature extent: the bf16 kernels address a 256-row tile
+// with 32-bit per-lane byte offsets that must stay below 1 GiB (256 x 2^20 x 2 bytes).
+constexpr int64_t kMaxExtent = int64_t(1) << 20;
+constexpr int64_t kMaxRows = int64_t(1) << 31;
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(TP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TP_OK;
+}
+
+#define TRY(expr)              \
+  do {                         \
+    const int _rc = (expr);    \
+    if (_rc != TP_OK) return _rc; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TPSHARD_ABI_VERSION; }
+
+const char* tp_last_error(void) { return g_err.c_str(); }
+
+int tp_shard_range(int64_t extent, int32_t T_p, int32_t t, int64_t* begin, int64_t* len) {
+  if (!begin || !len) return fail(TP_ERR_INVALID_ARG, "tp_shard_range: null output pointer");
+  if (T_p < 1) return fail(TP_ERR_INVALID_ARG, "tp_shard_range: T_p=%d < 1", T_p);
+  if (t < 0 || t >= T_p) return fail(TP_ERR_INVALID_ARG, "tp_shard_range: rank t=%d outside [0, %d)", t, T_p);
+  if (extent < 0) return fail(TP_ERR_INVALID_ARG, "tp_shard_range: negative extent %lld", (long long)extent);
+  if (extent % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "tp_shard_range: extent %lld not divisible by T_p=%d",
+                (long long)extent, T_p);
+  const int64_t n = extent / T_p;
+  *begin = (int64_t)t * n;
+  *len = n;
+  return TP_OK;
+}
+
+size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_dtype) {
+  if (T < 0 || d_ff <= 0 || T_p < 1 || d_ff % T_p) return 0;
+  if (in_dtype != TP_F32 && in_dtype != TP_BF16) return 0;
+  const size_t elt = in_dtype == TP_BF16 ? 2 : 4;
+  return round256((size_t)T * (size_t)(d_ff / T_p) * elt);
+}
+
+int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* w2, void* y_t,
+                     void* workspace, size_t workspace_bytes, int64_t T, int64_t d, int64_t d_ff,
+                     int32_t T_p, int32_t t, int32_t act, int32_t in_dtype, int32_t out_dtype,
+                     void* hip_stream) {
+  if (T < 0 || T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: T=%lld out of range", (long long)T);
+  if (d <= 0 || d_ff <= 0) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: d and d_ff must be positive");
+  if (d > kMaxExtent || d_ff > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: d or d_ff above %lld", (long long)kMaxExtent);
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: rank t=%d outside [0, T_p=%d)", t, T_p);
+  if (d_ff % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "tp_ffn_shard_fwd: d_ff=%lld not divisible by T_p=%d", (long long)d_ff, T_p);
+  if (act < TP_ACT_NONE || act > TP_ACT_BILINEAR)
+    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: unknown activation %d", act);
+  const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
+  const bool bf = in_dtype == TP_BF16;
+  if (!((in_dtype == TP_BF16 && (out_dtype == TP_BF16 || out_dtype == TP_F32)) ||
+        (in_dtype == TP_F32 && out_dtype == TP_F32)))
+    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: dtype pair (in=%d, out=%d) not supported", in_dtype, out_dtype);
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w1, "w1"));
+  TRY(check_ptr(w2, "w2"));
+  TRY(check_ptr(y_t, "y_t"));
+  if (gated) TRY(check_ptr(w3, "w3"));
+  else if (w3) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: w3 given for a non-gated activation");
+  const int64_t n = d_ff / T_p;
+  const int vec = bf ? 8 : 4;
+  if (d % vec || n % vec || d_ff % vec)
+    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: d=%lld, d_ff=%lld and d_ff/T_p=%lld must be multiples of %d",
+                (long long)d, (long long)d_ff, (long long)n, vec);
+  const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
+  if (T > 0) {
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace is NULL");
+    if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
+  if (T == 0) return TP_OK;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const size_t elt = bf ? 2 : 4;
+
+  // Column-parallel GEMM: H(t) = act(X . W1[:, t*n : (t+1)*n] (, X . W3[:, ...]))
+  tpk::GemmDesc g1{};
+  g1.A = x;
+  g1.B0 = (const char*)w1 + (size_t)t * n * elt;
+  g1.B1 = gated ? (const char*)w3 + (size_t)t * n * elt : nullptr;
+  g1.C = workspace;
+  g1.M = T;
+  g1.N = (int32_t)n;
+  g1.K = (int32_t)d;
+  g1.lda = (int32_t)d;
+  g1.ldb = (int32_t)d_ff;
+  g1.ldc = (int32_t)n;
+  g1.act = act;
+  g1.out_f32 = !bf;
+  TRY(hip_status(bf ? tpk::launch_gemm_bf16(g1, s) : tpk::launch_gemm_f32(g1, s), "column-parallel GEMM launch"));
+
+  // Row-parallel GEMM: y(t) = H(t) . W2[t*n : (t+1)*n, :]
+  tpk::GemmDesc g2{};
+  g2.A = workspace;
+  g2.B0 = (const char*)w2 + (size_t)t * n * (size_t)d * elt;
+  g2.B1 = nullptr;
+  g2.C = y_t;
+  g2.M = T;
+  g2.N = (int32_t)d;
+  g2.K = (int32_t)n;
+  g2.lda = (int32_t)n;
+  g2.ldb = (int32_t)d;
+  g2.ldc = (int32_t)d;
+  g2.act = TP_ACT_NONE;
+  g2.out_f32 = out_dtype == TP_F32;
+  return hip_status(bf ? tpk::launch_gemm_bf16(g2, s) : tpk::launch_gemm_f32(g2, s), "row-parallel GEMM launch");
+}
+
+int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t, int64_t T, int64_t d,
+                              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t T_p,
+                              int32_t t, int32_t in_dtype, int32_t out_dtype, void* hip_stream) {
+  if (T < 0 || T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "tp_attn_outproj_shard_fwd: T out of range");
+  if (d <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return fail(TP_ERR_INVALID_ARG, "tp_attn_outproj_shard_fwd: d, head counts and head_dim must be positive");
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "tp_attn_outproj_shard_fwd: rank t=%d outside [0, T_p=%d)", t, T_p);
+  if (n_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+  if (n_kv_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+  if (n_heads % n_kv_heads)
+    return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
+  if (!((in_dtype == TP_BF16 && (out_dtype == TP_BF16 || out_dtype == TP_F32)) ||
+        (in_dtype == TP_F32 && out_dtype == TP_F32)))
+    return fail(TP_ERR_UNSUPPORTED, "tp_attn_outproj_shard_fwd: dtype pair (in=%d, out=%d) not supported", in_dtype, out_dtype);
+  const bool bf = in_dtype == TP_BF16;
+  const int64_t kdim = (int64_t)(n_heads / T_p) * head_dim;
+  const int vec = bf ? 8 : 4;
+  if (d % vec || kdim % vec)
+    return fail(TP_ERR_UNSUPPORTED, "tp_attn_outproj_shard_fwd: d and h_t*head_dim must be multiples of %d", vec);
+  if (d > kMaxExtent || (int64_t)n_heads * head_dim > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "tp_attn_outproj_shard_fwd: extent too large");
+  TRY(check_ptr(o_t, "o_t"));
+  TRY(check_ptr(wo, "wo"));
+  TRY(check_ptr(y_t, "y_t"));
+  if (T == 0) return TP_OK;
+  const size_t elt = bf ? 2 : 4;
+  tpk::GemmDesc g{};
+  g.A = o_t;
+  g.B0 = (const char*)wo + (size_t)t * (size_t)kdim * (size_t)d * elt;
+  g.B1 = nullptr;
+  g.C = y_t;
+  g.M = T;
+  g.N = (int32_t)d;
+  g.K = (int32_t)kdim;
+  g.lda = (int32_t)kdim;
+  g.ldb = (int32_t)d;
+  g.ldc = (int32_t)d;
+  g.act = TP_ACT_NONE;
+  g.out_f32 = out_dtype == TP_F32;
+  hipStream_t s = (hipStream_t)hip_stream;
+  return hip_status(bf ? tpk::launch_gemm_bf16(g, s) : tpk::launch_gemm_f32(g, s), "out-projection GEMM launch");
+}
+
+size_t tp_attn_heads_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t T_p) {
+  if (n_seq < 0 || seq_len < 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || T_p < 1) return 0;
+  if (n_heads % T_p || n_kv_heads % T_p) return 0;
+  const int64_t h_t = n_heads / T_p, kv_t = n_kv_heads / T_p;
+  return round256((size_t)(n_seq * seq_len) * (size_t)((h_t + 2 * kv_t) * head_dim) * 2);
+}
+
+int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                            void* o_t, void* workspace, size_t workspace_bytes, int64_t n_seq,
+                            int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t T_p, int32_t t, int32_t causal,
+                            void* hip_stream) {
+  (void)x; (void)wq; (void)wk; (void)wv; (void)o_t; (void)workspace; (void)workspace_bytes;
+  (void)n_seq; (void)seq_len; (void)d; (void)n_heads; (void)n_kv_heads; (void)head_dim;
+  (void)T_p; (void)t; (void)causal; (void)hip_stream;
+  return fail(TP_ERR_UNSUPPORTED, "tp_attn_heads_shard_fwd: not built yet");
+}
+
+int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, const void* residual,
+                   void* y, int64_t n_elems, int32_t part_dtype, int32_t out_dtype, void* hip_stream) {
+  if (T_p < 1) return fail(TP_ERR_INVALID_ARG, "tp_partial_sum: T_p=%d < 1", T_p);
+  if (n_elems < 0) return fail(TP_ERR_INVALID_ARG, "tp_partial_sum: negative n_elems");
+  if ((part_dtype != TP_F32 && part_dtype != TP_BF16) || (out_dtype != TP_F32 && out_dtype != TP_BF16))
+    return fail(TP_ERR_UNSUPPORTED, "tp_partial_sum: dtypes (%d, %d) not supported", part_dtype, out_dtype);
+  if (partial_stride < n_elems)
+    return fail(TP_ERR_INVALID_ARG, "tp_partial_sum: partial_stride %lld < n_elems %lld",
+                (long long)partial_stride, (long long)n_elems);
+  if (T_p > 1 && partial_stride % 8)
+    return fail(TP_ERR_UNSUPPORTED, "tp_partial_sum: partial_stride must be a multiple of 8 elements");
+  TRY(check_ptr(partials, "partials"));
+  TRY(check_ptr(y, "y"));
+  if (residual) TRY(check_ptr(residual, "residual"));
+  const size_t pe = part_dtype == TP_BF16 ? 2 : 4, oe = out_dtype == TP_BF16 ? 2 : 4;
+  const uintptr_t p0 = (uintptr_t)partials, p1 = p0 + (uintptr_t)((T_p - 1) * partial_stride + n_elems) * pe;
+  const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)n_elems * oe;
+  if (n_elems > 0 && y0 < p1 && p0 < y1)
+    return fail(TP_ERR_INVALID_ARG, "tp_partial_sum: y overlaps the partials");
+  if (n_elems == 0) return TP_OK;
+  return hip_status(tpk::launch_partial_sum(partials, partial_stride, T_p, residual, y, n_elems,
+                                            part_dtype == TP_BF16, out_dtype == TP_BF16,
+                                            (hipStream_t)hip_stream),
+                    "partial-sum launch");
+}
+
+}  // extern "C"

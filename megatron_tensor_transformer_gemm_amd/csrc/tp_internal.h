@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (capi.hip) and the kernel files.
+// Launchers enqueue on the given stream and return hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum Act : int { kActNone = 0, kActGelu = 1, kActSwiglu = 2, kActBilinear = 3 };
+
+// C[M, N] = epilogue(A[M, K] . B0[K, N] (, A . B1[K, N])), all row-major.
+// B0/B1 point at the first element of the rank's block (offsets already applied).
+struct GemmDesc {
+  const void* A;
+  const void* B0;
+  const void* B1;  // only for the gated activations (SwiGLU, bilinear)
+  void* C;
+  int64_t M;
+  int32_t N, K;
+  int32_t lda, ldb, ldc;
+  int act;
+  bool out_f32;
+};
+
+// bf16 inputs, fp32 accumulation on MFMA; output bf16 (or fp32 if out_f32).
+hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t s);
+// fp32 inputs and output.
+hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t s);
+
+// y = sum_t parts[t*stride + i] (+ res[i]); dtypes: 0 = f32, 1 = bf16.
+hipError_t launch_partial_sum(const void* parts, int64_t stride, int T_p, const void* res,
+                              void* y, int64_t n, int part_bf16, int out_bf16, hipStream_t s);
+
+// Causal / full attention over head-major Q, K, V^T blocks (see attention.hip).
+struct AttnDesc {
+  const __bf16* q;   // [n_seq*seq_len, ldq] rows, head j at column j*head_dim
+  const __bf16* k;   // [n_seq*seq_len, ldk] rows, kv head at column kv*head_dim
+  const __bf16* vt;  // [kv_t][n_seq][head_dim][seq_len]  (V transposed per head/sequence)
+  __bf16* o;         // [n_seq*seq_len, ldo]
+  int64_t n_seq;
+  int32_t seq_len, head_dim, h_t, kv_t;
+  int32_t ldq, ldk, ldo;
+  bool causal;
+};
+hipError_t launch_attention(const AttnDesc& a, hipStream_t s);
+
+}  // namespace tpk

@@ -1,0 +1,124 @@
+"""Host side of the C ABI, without a GPU: the library loads, exports every function
+the header declares, and rejects invalid calls before launching anything.
+
+Every call below is invalid in at least one argument that is checked before any
+kernel launch, so the fake device addresses are never dereferenced.
+"""
+from __future__ import annotations
+
+import pytest
+
+from megatron_tensor_transformer_gemm_amd import tpshard as S
+from oracle import tp_oracle as O
+
+P = 0x100000          # fake, 16-byte aligned "device" address (never dereferenced)
+MIS = 0x100008        # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return S.lib()
+
+
+def test_library_exports_every_declared_function(L):
+    names = S.header_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert S.tp_abi_version() == 1
+
+
+@pytest.mark.parametrize("extent,T_p", [(14336, 8), (28672, 8), (4096, 4), (27720, 11), (0, 3),
+                                        (1024, 2), (6144, 8)])
+def test_shard_range_matches_oracle(extent, T_p):
+    for t in range(T_p):
+        assert S.tp_shard_range(extent, T_p, t) == O.shard_range(extent, T_p, t)
+
+
+@pytest.mark.parametrize("args,code", [((10, 3, 0), S.TP_ERR_NOT_DIVISIBLE), ((8, 0, 0), S.TP_ERR_INVALID_ARG),
+                                       ((8, 2, 2), S.TP_ERR_INVALID_ARG), ((8, 2, -1), S.TP_ERR_INVALID_ARG),
+                                       ((-8, 2, 0), S.TP_ERR_INVALID_ARG)])
+def test_shard_range_errors(args, code):
+    with pytest.raises(S.TPError) as e:
+        S.tp_shard_range(*args)
+    assert e.value.code == code
+    assert S.tp_last_error()
+
+
+def test_workspace_queries():
+    assert S.tp_ffn_workspace_bytes(8192, 14336, 8, S.TP_BF16) == 8192 * 1792 * 2
+    assert S.tp_ffn_workspace_bytes(3, 24, 8, S.TP_BF16) == 256          # rounded up
+    assert S.tp_ffn_workspace_bytes(64, 1024, 2, S.TP_F32) == 64 * 512 * 4
+    assert S.tp_ffn_workspace_bytes(64, 1000, 3, S.TP_BF16) == 0
+    assert S.tp_ffn_workspace_bytes(64, 1024, 2, 7) == 0
+    assert S.tp_attn_heads_workspace_bytes(1, 2048, 48, 48, 128, 8) == 2048 * 18 * 128 * 2
+    assert S.tp_attn_heads_workspace_bytes(1, 2048, 64, 8, 128, 16) == 0
+
+
+def _ffn(**kw):
+    a = dict(x=P, w1=P, w3=None, w2=P, y_t=P, workspace=P, workspace_bytes=1 << 30, T=64, d=256,
+             d_ff=1024, T_p=2, t=0, act=S.TP_ACT_GELU, in_dtype=S.TP_BF16, out_dtype=S.TP_BF16,
+             hip_stream=0)
+    a.update(kw)
+    return S.tp_ffn_shard_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), S.TP_ERR_INVALID_ARG),
+    (dict(w2=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(d_ff=1000, T_p=3), S.TP_ERR_NOT_DIVISIBLE),
+    (dict(T_p=0), S.TP_ERR_INVALID_ARG),
+    (dict(t=2), S.TP_ERR_INVALID_ARG),
+    (dict(T=-1), S.TP_ERR_INVALID_ARG),
+    (dict(d=0), S.TP_ERR_INVALID_ARG),
+    (dict(act=S.TP_ACT_SWIGLU), S.TP_ERR_INVALID_ARG),          # SwiGLU without W3
+    (dict(w3=P), S.TP_ERR_INVALID_ARG),                          # W3 with GELU
+    (dict(act=9), S.TP_ERR_UNSUPPORTED),
+    (dict(in_dtype=S.TP_F32, out_dtype=S.TP_BF16), S.TP_ERR_UNSUPPORTED),
+    (dict(d=260), S.TP_ERR_UNSUPPORTED),                         # not a multiple of 8 (bf16)
+    (dict(d_ff=1020, T_p=5), S.TP_ERR_UNSUPPORTED),              # n = 204: not a multiple of 8
+    (dict(workspace_bytes=100), S.TP_ERR_WORKSPACE),
+    (dict(workspace=None), S.TP_ERR_WORKSPACE),
+    (dict(d=(1 << 20) + 8), S.TP_ERR_UNSUPPORTED),               # beyond the supported extent
+])
+def test_ffn_rejects_before_launch(kw, code):
+    with pytest.raises(S.TPError) as e:
+        _ffn(**kw)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_kv_heads=8, T_p=16), S.TP_ERR_NOT_DIVISIBLE),         # GQA: 8 KV heads cap TP at 8
+    (dict(n_heads=48, n_kv_heads=48, T_p=5), S.TP_ERR_NOT_DIVISIBLE),
+    (dict(t=8), S.TP_ERR_INVALID_ARG),
+    (dict(o_t=None), S.TP_ERR_INVALID_ARG),
+    (dict(n_heads=64, n_kv_heads=24, T_p=8), S.TP_ERR_INVALID_ARG),
+    (dict(in_dtype=S.TP_F32, out_dtype=S.TP_BF16), S.TP_ERR_UNSUPPORTED),
+])
+def test_outproj_rejects_before_launch(kw, code):
+    a = dict(o_t=P, wo=P, y_t=P, T=16, d=8192, n_heads=64, n_kv_heads=8, head_dim=128, T_p=8, t=0,
+             in_dtype=S.TP_BF16, out_dtype=S.TP_BF16, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_outproj_shard_fwd(**a)
+    assert e.value.code == code, S.tp_last_error()
+    if "n_kv_heads" in kw and kw.get("T_p") == 16:
+        assert "n_kv_heads" in S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T_p=0), S.TP_ERR_INVALID_ARG),
+    (dict(partial_stride=10), S.TP_ERR_INVALID_ARG),
+    (dict(partial_stride=1001), S.TP_ERR_UNSUPPORTED),
+    (dict(y=P + 16), S.TP_ERR_INVALID_ARG),                      # overlaps the partials
+    (dict(part_dtype=5), S.TP_ERR_UNSUPPORTED),
+    (dict(n_elems=-1), S.TP_ERR_INVALID_ARG),
+    (dict(residual=MIS), S.TP_ERR_INVALID_ARG),
+])
+def test_partial_sum_rejects_before_launch(kw, code):
+    a = dict(partials=P, partial_stride=1000, T_p=4, residual=None, y=P + (1 << 24), n_elems=1000,
+             part_dtype=S.TP_BF16, out_dtype=S.TP_BF16, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_partial_sum(**a)
+    assert e.value.code == code, S.tp_last_error()
