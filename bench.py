@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel step on one MI355X.
+
+A step is one pass of the whole hot path over the Llama-3-70B-shaped
+workload (T = 16384 tokens, d = 8192, d_ff = 28672, T_p = 8; 64 query / 8 KV
+heads of 128): for every rank t of the T_p ranks held on this one GPU,
+    column-parallel GEMM  H(t) = silu(X W1(t)) * (X W3(t))   (activation fused)
+    row-parallel GEMM     y(t) = H(t) W2(t)                   (partial sum)
+then the local partial sum y = sum_t y(t) standing in for the all-reduce; then
+the row-sharded attention output projection a(t) = O(t) Wo(t) for every rank
+and its partial sum.  Inputs are seeded synthetic tensors resident in HBM
+before timing starts.
+
+Prints one JSON line.  value = algorithmic GEMM FLOPs of the step (2MNK per
+product) / measured step time.  Per-kernel durations come from HIP events
+recorded between the kernels on the stream they run on; the roofline object
+describes the dominant kernel (the column-parallel GEMM with the SwiGLU
+epilogue).  The CPU baseline is the float64 oracle timed on a bounded sample of
+the same workload (a subset of token rows, all ranks), and the sampled rows of
+the GPU result are compared with it (max_err).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TOL = 2e-2                    # normwise max relative error, bf16 with fp32 accumulation
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "megatron_tensor_transformer_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, per_launch_units: float):
+    """HBM traffic of the dominant kernel from the committed PMC summary, if it still
+    describes the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="token rows of the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: every tensor-parallel "
+                                   "rank's shard runs on that GPU and a local partial sum stands "
+                                   "in for the all-reduce; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from megatron_tensor_transformer_gemm_amd import tpshard as S
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    torch.cuda.set_device(0)
+    S.lib()  # fail now if the HIP library is not built
+
+    w = I.WORKLOADS[4]
+    T, d, d_ff, T_p = w.T, w.d, w.d_ff, w.T_p
+    n = d_ff // T_p
+    h_t = w.n_heads // T_p
+    kdim = h_t * w.head_dim
+    log(f"[bench] workload {w.name}: T={T} d={d} d_ff={d_ff} T_p={T_p}; generating inputs")
+    t0 = time.perf_counter()
+    host = {k: I.make_tensor(w, k) for k in ("x", "w1", "w3", "w2", "wo", "o")}
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    X, W1, W3, W2, WO = (dev(host[k]) for k in ("x", "w1", "w3", "w2", "wo"))
+    O_t = [dev(host["o"][:, t * kdim:(t + 1) * kdim]) for t in range(T_p)]
+    H = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((T_p, T, d), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    A = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    BF = S.TP_BF16
+    n_kernels = 2 * T_p + 1 + T_p + 1
+    names = []
+    for _ in range(T_p):
+        names += ["col", "row"]
+    names += ["psum"] + ["outproj"] * T_p + ["psum"]
+    assert len(names) == n_kernels
+
+    def step(evs=None):
+        k = 0
+        if evs:
+            evs[0].record()
+        for t in range(T_p):
+            S.tp_ffn_column_fwd(X, W1, W3, H, T, d, d_ff, T_p, t, S.TP_ACT_SWIGLU, BF)
+            if evs:
+                k += 1
+                evs[k].record()
+            S.tp_ffn_row_fwd(H, W2, P[t], T, d, d_ff, T_p, t, BF, BF)
+            if evs:
+                k += 1
+                evs[k].record()
+        S.tp_partial_sum(P, T * d, T_p, None, Y, T * d, BF, BF)
+        if evs:
+            k += 1
+            evs[k].record()
+        for t in range(T_p):
+            S.tp_attn_outproj_shard_fwd(O_t[t], WO, P[t], T, d, w.n_heads, w.n_kv_heads,
+                                        w.head_dim, T_p, t, BF, BF)
+            if evs:
+                k += 1
+                evs[k].record()
+        S.tp_partial_sum(P, T * d, T_p, None, A, T * d, BF, BF)
+        if evs:
+            k += 1
+            evs[k].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    dur = {}  # kernel name -> list of ms
+    for s in range(args.steps):
+        for i, nm in enumerate(names):
+            dur.setdefault(nm, []).append(ev[s][i].elapsed_time(ev[s][i + 1]))
+    avg_us = {k: 1e3 * sum(v) / len(v) for k, v in dur.items()}
+
+    fl_col = 2.0 * T * d * n * 2
+    fl_row = 2.0 * T * n * d
+    fl_out = 2.0 * T * kdim * d
+    step_flops = T_p * (fl_col + fl_row + fl_out)
+    psum_bytes = (T_p + 1) * T * d * 2
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    def tfl(fl, us):
+        return fl / (us * 1e-6) / 1e12
+
+    kernels = {
+        "column_gemm_swiglu": {"avg_us": round(avg_us["col"], 2),
+                               "tflops": round(tfl(fl_col, avg_us["col"]), 1),
+                               "frac_peak": round(tfl(fl_col, avg_us["col"]) / PEAK_BF16_TFLOPS, 4),
+                               "launches_per_step": T_p},
+        "row_gemm": {"avg_us": round(avg_us["row"], 2),
+                     "tflops": round(tfl(fl_row, avg_us["row"]), 1),
+                     "frac_peak": round(tfl(fl_row, avg_us["row"]) / PEAK_BF16_TFLOPS, 4),
+                     "launches_per_step": T_p},
+        "attn_outproj_gemm": {"avg_us": round(avg_us["outproj"], 2),
+                              "tflops": round(tfl(fl_out, avg_us["outproj"]), 1),
+                              "frac_peak": round(tfl(fl_out, avg_us["outproj"]) / PEAK_BF16_TFLOPS, 4),
+                              "launches_per_step": T_p},
+        "partial_sum": {"avg_us": round(avg_us["psum"], 2),
+                        "gbs": round(psum_bytes / (avg_us["psum"] * 1e-6) / 1e9, 1),
+                        "frac_peak": round(psum_bytes / (avg_us["psum"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "launches_per_step": 2},
+    }
+    col_tf = tfl(fl_col, avg_us["col"])
+    roofline = {"bound": "mfma", "achieved": round(col_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(col_tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("column_gemm_swiglu", w.name, fl_col),
+                "kernel": "column-parallel GEMM + SwiGLU epilogue (per rank)",
+                "flops_per_launch": fl_col}
+
+    out = {
+        "metric": "TP-shard FFN fwd TFLOP/s (bf16, 1 GPU) + % of MFMA peak; oracle-match max err",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "d": d, "d_ff": d_ff, "T_p": T_p,
+                   "ranks_per_step": T_p, "act": "swiglu", "n_heads": w.n_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "parallelism": f"tp{T_p} ranks emulated on 1 GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "step_gemm_flops": step_flops,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        out.update(cpu_baseline(host, w, Y, A, args.cpu_rows))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
+    """Time the float64 oracle on a sample of token rows (all ranks, both sublayers) and
+    compare the GPU's reduced outputs at those rows."""
+    import numpy as np
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from oracle import tp_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    T, d, T_p = w.T, w.d, w.T_p
+    n = w.d_ff // T_p
+    kdim = w.n_heads // T_p * w.head_dim
+    g = np.random.default_rng(1234)
+    rows = np.unique(np.concatenate([[0, T - 1], g.choice(T, size=rows_n - 2, replace=False)]))
+    R = len(rows)
+    log(f"[bench] CPU oracle on {R} token rows, {cores} BLAS threads")
+    # decode the bf16 inputs once (exact values); the oracle widens its slices to float64
+    xs = I.as_f64(host["x"][rows], w.dtype)
+    os_ = I.as_f64(host["o"][rows], w.dtype)
+    w1, w3, w2, wo = (I.bf16_to_f32(host[k]) for k in ("w1", "w3", "w2", "wo"))
+    t0 = time.perf_counter()
+    y_parts, a_parts = [], []
+    for t in range(T_p):
+        _, y_t = O.ffn_shard(xs, w1, w3, w2, T_p, t, w.act)
+        y_parts.append(y_t)
+        a_parts.append(O.attn_outproj_shard(os_[:, t * kdim:(t + 1) * kdim], wo, w.n_heads,
+                                            w.n_kv_heads, w.head_dim, T_p, t))
+    y_ref = O.partial_sum(y_parts)
+    a_ref = O.partial_sum(a_parts)
+    cpu_s = time.perf_counter() - t0
+    flops = T_p * R * (2.0 * d * n * 3 + 2.0 * kdim * d)
+    yg = Y[rows].float().cpu().numpy()
+    ag = A[rows].float().cpu().numpy()
+    e_y = O.normwise_max_rel_err(yg, y_ref)
+    e_a = O.normwise_max_rel_err(ag, a_ref)
+    log(f"[bench] oracle {cpu_s:.1f} s; max err ffn {e_y:.3e} attn {e_a:.3e}")
+    return {
+        "cpu_baseline": {"value": round(flops / cpu_s / 1e12, 4), "unit": "TFLOP/s", "cores": cores,
+                         "kind": "oracle", "seconds": round(cpu_s, 2),
+                         "sample": f"{R} of {T} token rows (seeded, incl. first and last); all "
+                                   f"{T_p} ranks' SwiGLU FFN shards and attention out-projection "
+                                   f"shards plus both partial sums, float64 NumPy"},
+        "max_err": {"ffn_sum": e_y, "attn_outproj_sum": e_a, "rows_checked": R,
+                    "tolerance": TOL, "pass": bool(e_y <= TOL and e_a <= TOL)},
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

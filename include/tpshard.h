@@ -121,6 +121,26 @@ int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* 
                      int32_t act, int32_t in_dtype, int32_t out_dtype, void* hip_stream);
 
 /*
+ * The two halves of tp_ffn_shard_fwd, for callers that schedule them
+ * separately (e.g. to overlap the previous sublayer's exchange with the
+ * column-parallel product, or to time each kernel).
+ *
+ * tp_ffn_column_fwd: h_t [T, d_ff/T_p] (in_dtype) = act(x . W1(t) [, x . W3(t)])
+ *   -- the column-parallel GEMM with the activation fused into its epilogue
+ *   ("7.9 Tensor and pipeline parallelism", section 2.1, h^(t)).
+ * tp_ffn_row_fwd: y_t [T, d] (out_dtype) = h_t . W2[cols(t), :]
+ *   -- the row-parallel GEMM producing the rank's partial sum (section 2.1, y^(t)).
+ * Arguments mean what they mean for tp_ffn_shard_fwd; h_t is caller-owned,
+ * 16-byte aligned, T*(d_ff/T_p) elements.
+ */
+int tp_ffn_column_fwd(const void* x, const void* w1, const void* w3, void* h_t,
+                      int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
+                      int32_t act, int32_t in_dtype, void* hip_stream);
+int tp_ffn_row_fwd(const void* h_t, const void* w2, void* y_t,
+                   int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
+                   int32_t in_dtype, int32_t out_dtype, void* hip_stream);
+
+/*
  * Row-sharded attention output projection of rank t: y_t = o_t . Wo[rows(t), :].
  *
  *   o_t   [T, h_t*head_dim]         in_dtype, the rank's heads' outputs, contiguous

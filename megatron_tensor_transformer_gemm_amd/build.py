@@ -42,6 +42,19 @@ def _run(cmd):
     return out
 
 
+def _check_stubs(objs) -> None:
+    """Every kernel a host launcher references must have its launch stub defined."""
+    nm = shutil.which("nm")
+    if not nm:
+        return
+    for o in objs:
+        out = subprocess.run([nm, "-C", "-u", o], capture_output=True, text=True).stdout
+        missing = [ln.strip() for ln in out.splitlines() if "__device_stub__" in ln]
+        if missing:
+            raise RuntimeError(f"{o}: kernel launch stubs not emitted by the host pass:\n"
+                               + "\n".join(missing[:8]))
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = _hipcc()
     bdir = os.path.join(PKG, "_build")
@@ -53,6 +66,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out, file=sys.stderr)
+    _check_stubs(objs)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -81,78 +81,133 @@ size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_d
   return round256((size_t)T * (size_t)(d_ff / T_p) * elt);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the FFN entry points.  `need_*` select which pointers are validated.
+int check_ffn(const char* fn, const void* x, const void* w1, const void* w3, const void* w2,
+              const void* h, const void* y, int64_t T, int64_t d, int64_t d_ff, int32_t T_p,
+              int32_t t, int32_t act, int32_t in_dtype, int32_t out_dtype, bool col, bool row) {
+  if (T < 0 || T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: T=%lld out of range", fn, (long long)T);
+  if (d <= 0 || d_ff <= 0) return fail(TP_ERR_INVALID_ARG, "%s: d and d_ff must be positive", fn);
+  if (d > kMaxExtent || d_ff > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "%s: d or d_ff above %lld", fn, (long long)kMaxExtent);
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
+  if (d_ff % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "%s: d_ff=%lld not divisible by T_p=%d", fn, (long long)d_ff, T_p);
+  if (col && (act < TP_ACT_NONE || act > TP_ACT_BILINEAR))
+    return fail(TP_ERR_UNSUPPORTED, "%s: unknown activation %d", fn, act);
+  if (!((in_dtype == TP_BF16 && (out_dtype == TP_BF16 || out_dtype == TP_F32)) ||
+        (in_dtype == TP_F32 && out_dtype == TP_F32)))
+    return fail(TP_ERR_UNSUPPORTED, "%s: dtype pair (in=%d, out=%d) not supported", fn, in_dtype, out_dtype);
+  if (col) {
+    const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
+    TRY(check_ptr(x, "x"));
+    TRY(check_ptr(w1, "w1"));
+    if (gated) TRY(check_ptr(w3, "w3"));
+    else if (w3) return fail(TP_ERR_INVALID_ARG, "%s: w3 given for a non-gated activation", fn);
+  }
+  if (row) {
+    TRY(check_ptr(w2, "w2"));
+    TRY(check_ptr(y, "y_t"));
+  }
+  if (h) TRY(check_ptr(h, col && !row ? "h_t" : "workspace"));
+  const int64_t n = d_ff / T_p;
+  const int vec = in_dtype == TP_BF16 ? 8 : 4;
+  if (d % vec || n % vec || d_ff % vec)
+    return fail(TP_ERR_UNSUPPORTED, "%s: d=%lld, d_ff=%lld and d_ff/T_p=%lld must be multiples of %d", fn,
+                (long long)d, (long long)d_ff, (long long)n, vec);
+  return TP_OK;
+}
+
+int launch_column(const void* x, const void* w1, const void* w3, void* h, int64_t T, int64_t d,
+                  int64_t d_ff, int32_t T_p, int32_t t, int32_t act, bool bf, hipStream_t s) {
+  const int64_t n = d_ff / T_p;
+  const size_t elt = bf ? 2 : 4;
+  const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
+  // H(t) = act(X . W1[:, t*n : (t+1)*n] (, X . W3[:, ...]))
+  tpk::GemmDesc g{};
+  g.A = x;
+  g.B0 = (const char*)w1 + (size_t)t * n * elt;
+  g.B1 = gated ? (const char*)w3 + (size_t)t * n * elt : nullptr;
+  g.C = h;
+  g.M = T;
+  g.N = (int32_t)n;
+  g.K = (int32_t)d;
+  g.lda = (int32_t)d;
+  g.ldb = (int32_t)d_ff;
+  g.ldc = (int32_t)n;
+  g.act = act;
+  g.out_f32 = !bf;
+  return hip_status(bf ? tpk::launch_gemm_bf16(g, s) : tpk::launch_gemm_f32(g, s), "column-parallel GEMM launch");
+}
+
+int launch_row(const void* h, const void* w2, void* y, int64_t T, int64_t d, int64_t d_ff, int32_t T_p,
+               int32_t t, bool bf, bool out_f32, hipStream_t s) {
+  const int64_t n = d_ff / T_p;
+  const size_t elt = bf ? 2 : 4;
+  // y(t) = H(t) . W2[t*n : (t+1)*n, :]
+  tpk::GemmDesc g{};
+  g.A = h;
+  g.B0 = (const char*)w2 + (size_t)t * n * (size_t)d * elt;
+  g.B1 = nullptr;
+  g.C = y;
+  g.M = T;
+  g.N = (int32_t)d;
+  g.K = (int32_t)n;
+  g.lda = (int32_t)n;
+  g.ldb = (int32_t)d;
+  g.ldc = (int32_t)d;
+  g.act = TP_ACT_NONE;
+  g.out_f32 = out_f32;
+  return hip_status(bf ? tpk::launch_gemm_bf16(g, s) : tpk::launch_gemm_f32(g, s), "row-parallel GEMM launch");
+}
+
+}  // namespace
+
+extern "C" {
+
 int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* w2, void* y_t,
                      void* workspace, size_t workspace_bytes, int64_t T, int64_t d, int64_t d_ff,
                      int32_t T_p, int32_t t, int32_t act, int32_t in_dtype, int32_t out_dtype,
                      void* hip_stream) {
-  if (T < 0 || T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: T=%lld out of range", (long long)T);
-  if (d <= 0 || d_ff <= 0) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: d and d_ff must be positive");
-  if (d > kMaxExtent || d_ff > kMaxExtent)
-    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: d or d_ff above %lld", (long long)kMaxExtent);
-  if (T_p < 1 || t < 0 || t >= T_p)
-    return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: rank t=%d outside [0, T_p=%d)", t, T_p);
-  if (d_ff % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "tp_ffn_shard_fwd: d_ff=%lld not divisible by T_p=%d", (long long)d_ff, T_p);
-  if (act < TP_ACT_NONE || act > TP_ACT_BILINEAR)
-    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: unknown activation %d", act);
-  const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
-  const bool bf = in_dtype == TP_BF16;
-  if (!((in_dtype == TP_BF16 && (out_dtype == TP_BF16 || out_dtype == TP_F32)) ||
-        (in_dtype == TP_F32 && out_dtype == TP_F32)))
-    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: dtype pair (in=%d, out=%d) not supported", in_dtype, out_dtype);
-  TRY(check_ptr(x, "x"));
-  TRY(check_ptr(w1, "w1"));
-  TRY(check_ptr(w2, "w2"));
-  TRY(check_ptr(y_t, "y_t"));
-  if (gated) TRY(check_ptr(w3, "w3"));
-  else if (w3) return fail(TP_ERR_INVALID_ARG, "tp_ffn_shard_fwd: w3 given for a non-gated activation");
-  const int64_t n = d_ff / T_p;
-  const int vec = bf ? 8 : 4;
-  if (d % vec || n % vec || d_ff % vec)
-    return fail(TP_ERR_UNSUPPORTED, "tp_ffn_shard_fwd: d=%lld, d_ff=%lld and d_ff/T_p=%lld must be multiples of %d",
-                (long long)d, (long long)d_ff, (long long)n, vec);
-  const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
+  TRY(check_ffn("tp_ffn_shard_fwd", x, w1, w3, w2, nullptr, y_t, T, d, d_ff, T_p, t, act, in_dtype,
+                out_dtype, true, true));
   if (T > 0) {
     if (!workspace) return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace is NULL");
     if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
     if (workspace_bytes < need)
       return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace %zu bytes < %zu needed", workspace_bytes, need);
   }
   if (T == 0) return TP_OK;
   hipStream_t s = (hipStream_t)hip_stream;
-  const size_t elt = bf ? 2 : 4;
+  const bool bf = in_dtype == TP_BF16;
+  TRY(launch_column(x, w1, w3, workspace, T, d, d_ff, T_p, t, act, bf, s));
+  return launch_row(workspace, w2, y_t, T, d, d_ff, T_p, t, bf, out_dtype == TP_F32, s);
+}
 
-  // Column-parallel GEMM: H(t) = act(X . W1[:, t*n : (t+1)*n] (, X . W3[:, ...]))
-  tpk::GemmDesc g1{};
-  g1.A = x;
-  g1.B0 = (const char*)w1 + (size_t)t * n * elt;
-  g1.B1 = gated ? (const char*)w3 + (size_t)t * n * elt : nullptr;
-  g1.C = workspace;
-  g1.M = T;
-  g1.N = (int32_t)n;
-  g1.K = (int32_t)d;
-  g1.lda = (int32_t)d;
-  g1.ldb = (int32_t)d_ff;
-  g1.ldc = (int32_t)n;
-  g1.act = act;
-  g1.out_f32 = !bf;
-  TRY(hip_status(bf ? tpk::launch_gemm_bf16(g1, s) : tpk::launch_gemm_f32(g1, s), "column-parallel GEMM launch"));
+int tp_ffn_column_fwd(const void* x, const void* w1, const void* w3, void* h_t, int64_t T, int64_t d,
+                      int64_t d_ff, int32_t T_p, int32_t t, int32_t act, int32_t in_dtype,
+                      void* hip_stream) {
+  if (!h_t) return fail(TP_ERR_INVALID_ARG, "tp_ffn_column_fwd: h_t is NULL");
+  TRY(check_ffn("tp_ffn_column_fwd", x, w1, w3, nullptr, h_t, nullptr, T, d, d_ff, T_p, t, act,
+                in_dtype, in_dtype, true, false));
+  if (T == 0) return TP_OK;
+  return launch_column(x, w1, w3, h_t, T, d, d_ff, T_p, t, act, in_dtype == TP_BF16,
+                       (hipStream_t)hip_stream);
+}
 
-  // Row-parallel GEMM: y(t) = H(t) . W2[t*n : (t+1)*n, :]
-  tpk::GemmDesc g2{};
-  g2.A = workspace;
-  g2.B0 = (const char*)w2 + (size_t)t * n * (size_t)d * elt;
-  g2.B1 = nullptr;
-  g2.C = y_t;
-  g2.M = T;
-  g2.N = (int32_t)d;
-  g2.K = (int32_t)n;
-  g2.lda = (int32_t)n;
-  g2.ldb = (int32_t)d;
-  g2.ldc = (int32_t)d;
-  g2.act = TP_ACT_NONE;
-  g2.out_f32 = out_dtype == TP_F32;
-  return hip_status(bf ? tpk::launch_gemm_bf16(g2, s) : tpk::launch_gemm_f32(g2, s), "row-parallel GEMM launch");
+int tp_ffn_row_fwd(const void* h_t, const void* w2, void* y_t, int64_t T, int64_t d, int64_t d_ff,
+                   int32_t T_p, int32_t t, int32_t in_dtype, int32_t out_dtype, void* hip_stream) {
+  if (!h_t) return fail(TP_ERR_INVALID_ARG, "tp_ffn_row_fwd: h_t is NULL");
+  TRY(check_ffn("tp_ffn_row_fwd", nullptr, nullptr, nullptr, w2, h_t, y_t, T, d, d_ff, T_p, t,
+                TP_ACT_NONE, in_dtype, out_dtype, false, true));
+  if (T == 0) return TP_OK;
+  return launch_row(h_t, w2, y_t, T, d, d_ff, T_p, t, in_dtype == TP_BF16, out_dtype == TP_F32,
+                    (hipStream_t)hip_stream);
 }
 
 int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t, int64_t T, int64_t d,

@@ -111,7 +111,11 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   static_assert(MB >= 1 && NBS >= 1 && A_LD >= 1 && B_LD >= 1, "tile too small");
   static_assert(CPR >= 8, "B sub-tile narrower than 64 columns");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  // One array per stage: the buffer->LDS copies into one stage and the fragment reads
+  // of the other are then provably disjoint, so no wait on the copies is inserted
+  // before the reads (the copies of stage k+1 overlap the products of stage k).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,56 +131,70 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   const __bf16* B0 = (const __bf16*)g.B0 + n0;
   const __bf16* B1 = DUAL ? (const __bf16*)g.B1 + n0 : B0;
 
-  // ---- per-lane global->LDS descriptors (fixed over the k loop)
+  // ---- per-lane global->LDS descriptors (fixed over the k loop).  Lanes whose row (A)
+  // or column (B) lies outside the matrix get an out-of-range offset once and for all;
+  // the k-tail is masked only in the last, partial k-tile.
   uint32_t a_voff[A_LD];
-  int a_k[A_LD];
-  bool a_ok[A_LD];
+  int a_kc[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = wave * A_LD + i;
     const int row = q * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz_a(row);
-    a_voff[i] = (uint32_t)(row * g.lda + 8 * c) * 2u;
-    a_k[i] = 8 * c;
-    a_ok[i] = row < rows_left;
+    a_voff[i] = row < rows_left ? (uint32_t)(row * g.lda + 8 * c) * 2u : kOOB;
+    a_kc[i] = 8 * c;
   }
   uint32_t b_voff[B_LD];
-  int b_row[B_LD];
-  bool b_ok[B_LD];
+  int b_kr[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int q = wave * B_LD + i;
     const int pos = (q % QSUB) * 64 + lane;
     const int row = pos / CPR;
     const int c = (pos % CPR) ^ (swz_b(row) & (CPR - 1));
-    b_voff[i] = (uint32_t)(row * g.ldb + 8 * c) * 2u;
-    b_row[i] = row;
-    b_ok[i] = n0 + 8 * c < g.N;
+    b_voff[i] = (n0 + 8 * c < g.N) ? (uint32_t)(row * g.ldb + 8 * c) * 2u : kOOB;
+    b_kr[i] = row;
   }
+  // B sub-tile a wave's copies land in is the same for all of its copies.
+  const bool b_second = (wave * B_LD) / QSUB != 0;
 
-  auto issue = [&](int kt, int stage) {
+  // (Each offset goes through a local before the builtin call: handing the builtin an
+  // element of a captured array directly makes the host compilation pass drop the
+  // kernel's launch stub.)
+  auto issue = [&](int kt, LDS_AS unsigned char* base) {
     const int k0 = kt * kBK;
-    LDS_AS unsigned char* base = (LDS_AS unsigned char*)smem + stage * STAGE;
+    const bool full = k0 + kBK <= g.K;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + k0);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc((b_second ? B1 : B0) + (int64_t)k0 * g.ldb);
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const uint32_t v = (a_ok[i] && (k0 + a_k[i] < g.K)) ? a_voff[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(base + (wave * A_LD + i) * 1024),
-                                               16, v, 0, 0, 0);
-    }
-    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + (int64_t)k0 * g.ldb);
-    const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(B1 + (int64_t)k0 * g.ldb);
+      for (int i = 0; i < A_LD; ++i) {
+        const uint32_t v = a_voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (LDS_AS void*)(base + (wave * A_LD + i) * 1024), 16, v, 0, 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = wave * B_LD + i;
-      const uint32_t v = (b_ok[i] && (k0 + b_row[i] < g.K)) ? b_voff[i] : kOOB;
-      LDS_AS void* dst = (LDS_AS void*)(base + A_BYTES + q * 1024);
-      if (q / QSUB == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, dst, 16, v, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, dst, 16, v, 0, 0, 0);
+      for (int i = 0; i < B_LD; ++i) {
+        const uint32_t v = b_voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (LDS_AS void*)(base + A_BYTES + (wave * B_LD + i) * 1024), 16, v, 0, 0, 0);
+      }
+    } else {  // last, partial k-tile
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) {
+        const uint32_t v = (k0 + a_kc[i] < g.K) ? a_voff[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (LDS_AS void*)(base + (wave * A_LD + i) * 1024), 16, v, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) {
+        const uint32_t v = (k0 + b_kr[i] < g.K) ? b_voff[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (LDS_AS void*)(base + A_BYTES + (wave * B_LD + i) * 1024), 16, v, 0, 0, 0);
+      }
     }
   };
+
 
   // ---- per-lane LDS read offsets
   const int arow = wm * WTM + (lane & 31);
@@ -205,35 +223,81 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-  const int nk = (g.K + kBK - 1) / kBK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
-    const LDS_AS unsigned char* As = (const LDS_AS unsigned char*)smem + st * STAGE;
+  // Fragments of k-substep s (16 k) of the stage at `As`.
+  auto load_frags = [&](const LDS_AS unsigned char* As, int s, bf16x8 (&af)[MB],
+                        bf16x8 (&bfr)[NB]) {
     const LDS_AS unsigned char* Bs = As + A_BYTES;
 #pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * 128);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
+      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+      bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // All products of one stage.  The fragments of substep s+1 are read while substep s
+  // multiplies: the scheduler is told to alternate one MFMA with one LDS read.
+  constexpr int NREAD = MB + 2 * NB;  // LDS reads per substep
+  constexpr int NMFMA = MB * NB;      // MFMAs per substep
+  constexpr int NPAIR = NMFMA < NREAD ? NMFMA : NREAD;
+  auto compute = [&](const LDS_AS unsigned char* As) {
+    bf16x8 af[2][MB];
+    bf16x8 bfr[2][NB];
+    load_frags(As, 0, af[0], bfr[0]);
+#pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 af[MB];
-      bf16x8 bfr[NB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * 128);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
-        bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
-        bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
-        bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      if (s < 3) load_frags(As, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][nb], af[s & 1][mb],
+                                                                 acc[mb][nb], 0, 0, 0);
     }
+    // schedule: reads of substep 0, then per substep one MFMA / one read pairs
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < NPAIR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
+        if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+      }
+    }
+  };
+
+  LDS_AS unsigned char* S0 = (LDS_AS unsigned char*)smem0;
+  LDS_AS unsigned char* S1 = (LDS_AS unsigned char*)smem1;
+  const int nk = (g.K + kBK - 1) / kBK;
+  issue(0, S0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(kt + 1, S1);                        // stays ahead of the products below
+    __builtin_amdgcn_sched_barrier(0);
+    compute(S0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < nk) issue(kt + 2, S0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(S1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kt < nk) {  // odd number of k-tiles: the last one sits in stage 0
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    compute(S0);
   }
 
   // ---- epilogue: activation on the fp32 accumulators, one rounding, vector stores

@@ -41,6 +41,8 @@ _SIGS = {
     "tp_ffn_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "tp_ffn_shard_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _i32,
                                 _i32, _i32, _i32, _vp]),
+    "tp_ffn_column_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
+    "tp_ffn_row_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "tp_attn_outproj_shard_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _vp]),
     "tp_attn_heads_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
@@ -132,6 +134,20 @@ def tp_ffn_shard_fwd(x, w1, w3, w2, y_t, workspace, workspace_bytes, T, d, d_ff,
     _check("tp_ffn_shard_fwd", lib().tp_ffn_shard_fwd(
         _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y_t), _ptr(workspace), workspace_bytes,
         T, d, d_ff, T_p, t, act, in_dtype, out_dtype, _stream(hip_stream)))
+
+
+def tp_ffn_column_fwd(x, w1, w3, h_t, T, d, d_ff, T_p, t, act, in_dtype, hip_stream=None):
+    if isinstance(act, str):
+        act = ACT[act]
+    _check("tp_ffn_column_fwd", lib().tp_ffn_column_fwd(
+        _ptr(x), _ptr(w1), _ptr(w3), _ptr(h_t), T, d, d_ff, T_p, t, act, in_dtype,
+        _stream(hip_stream)))
+
+
+def tp_ffn_row_fwd(h_t, w2, y_t, T, d, d_ff, T_p, t, in_dtype, out_dtype, hip_stream=None):
+    _check("tp_ffn_row_fwd", lib().tp_ffn_row_fwd(
+        _ptr(h_t), _ptr(w2), _ptr(y_t), T, d, d_ff, T_p, t, in_dtype, out_dtype,
+        _stream(hip_stream)))
 
 
 def tp_attn_outproj_shard_fwd(o_t, wo, y_t, T, d, n_heads, n_kv_heads, head_dim, T_p, t,

@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 1
