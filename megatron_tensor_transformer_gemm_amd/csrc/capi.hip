@@ -269,10 +269,83 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
                             int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
                             int32_t head_dim, int32_t T_p, int32_t t, int32_t causal,
                             void* hip_stream) {
-  (void)x; (void)wq; (void)wk; (void)wv; (void)o_t; (void)workspace; (void)workspace_bytes;
-  (void)n_seq; (void)seq_len; (void)d; (void)n_heads; (void)n_kv_heads; (void)head_dim;
-  (void)T_p; (void)t; (void)causal; (void)hip_stream;
-  return fail(TP_ERR_UNSUPPORTED, "tp_attn_heads_shard_fwd: not built yet");
+  const char* fn = "tp_attn_heads_shard_fwd";
+  if (n_seq < 0 || seq_len < 0 || n_seq > 65535)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_seq=%lld / seq_len=%lld out of range", fn, (long long)n_seq,
+                (long long)seq_len);
+  if (d <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: d, head counts and head_dim must be positive", fn);
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
+  if (n_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+  if (n_kv_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+  if (n_heads % n_kv_heads)
+    return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TP_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", fn, head_dim);
+  if (causal != 0 && causal != 1) return fail(TP_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  if (d % 8) return fail(TP_ERR_UNSUPPORTED, "%s: d must be a multiple of 8", fn);
+  if (d > kMaxExtent || (int64_t)n_heads * head_dim > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "%s: extent too large", fn);
+  const int64_t T = n_seq * seq_len;
+  if (T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: too many tokens", fn);
+  const int64_t h_t = n_heads / T_p, kv_t = n_kv_heads / T_p;
+  // the attention kernel addresses one sequence of a head with 32-bit byte offsets
+  if ((int64_t)seq_len * (h_t + 2 * kv_t) * head_dim * 2 >= (int64_t(1) << 30))
+    return fail(TP_ERR_UNSUPPORTED, "%s: seq_len too long for one call", fn);
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(wq, "wq"));
+  TRY(check_ptr(wk, "wk"));
+  TRY(check_ptr(wv, "wv"));
+  TRY(check_ptr(o_t, "o_t"));
+  const size_t need = tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
+  if (T > 0) {
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+    if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  }
+  if (T == 0) return TP_OK;
+  hipStream_t s = (hipStream_t)hip_stream;
+  __bf16* q = (__bf16*)workspace;
+  __bf16* k = q + T * h_t * head_dim;
+  __bf16* v = k + T * kv_t * head_dim;
+  // Q, K, V column blocks of the rank's heads (column-parallel projections, no activation)
+  struct Proj { const void* w; __bf16* out; int64_t heads_total, heads_rank; } proj[3] = {
+      {wq, q, n_heads, h_t}, {wk, k, n_kv_heads, kv_t}, {wv, v, n_kv_heads, kv_t}};
+  for (const Proj& p : proj) {
+    tpk::GemmDesc g{};
+    g.A = x;
+    g.B0 = (const __bf16*)p.w + (size_t)t * p.heads_rank * head_dim;
+    g.B1 = nullptr;
+    g.C = p.out;
+    g.M = T;
+    g.N = (int32_t)(p.heads_rank * head_dim);
+    g.K = (int32_t)d;
+    g.lda = (int32_t)d;
+    g.ldb = (int32_t)(p.heads_total * head_dim);
+    g.ldc = g.N;
+    g.act = TP_ACT_NONE;
+    g.out_f32 = false;
+    TRY(hip_status(tpk::launch_gemm_bf16(g, s), "QKV projection GEMM launch"));
+  }
+  tpk::AttnDesc a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = (__bf16*)o_t;
+  a.n_seq = n_seq;
+  a.seq_len = (int32_t)seq_len;
+  a.head_dim = head_dim;
+  a.h_t = (int32_t)h_t;
+  a.kv_t = (int32_t)kv_t;
+  a.ldq = (int32_t)(h_t * head_dim);
+  a.ldkv = (int32_t)(kv_t * head_dim);
+  a.ldo = (int32_t)(h_t * head_dim);
+  a.causal = causal != 0;
+  return hip_status(tpk::launch_attention(a, s), "attention launch");
 }
 
 int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, const void* residual,

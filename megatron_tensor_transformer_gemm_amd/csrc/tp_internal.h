@@ -32,15 +32,16 @@ hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t s);
 hipError_t launch_partial_sum(const void* parts, int64_t stride, int T_p, const void* res,
                               void* y, int64_t n, int part_bf16, int out_bf16, hipStream_t s);
 
-// Causal / full attention over head-major Q, K, V^T blocks (see attention.hip).
+// Scaled dot-product attention of a rank's heads (see attention.hip).  Q, K, V and O
+// are token-row-major; head j occupies columns [j*head_dim, (j+1)*head_dim).
 struct AttnDesc {
-  const __bf16* q;   // [n_seq*seq_len, ldq] rows, head j at column j*head_dim
-  const __bf16* k;   // [n_seq*seq_len, ldk] rows, kv head at column kv*head_dim
-  const __bf16* vt;  // [kv_t][n_seq][head_dim][seq_len]  (V transposed per head/sequence)
+  const __bf16* q;   // [n_seq*seq_len, ldq]
+  const __bf16* k;   // [n_seq*seq_len, ldkv]
+  const __bf16* v;   // [n_seq*seq_len, ldkv]
   __bf16* o;         // [n_seq*seq_len, ldo]
   int64_t n_seq;
   int32_t seq_len, head_dim, h_t, kv_t;
-  int32_t ldq, ldk, ldo;
+  int32_t ldq, ldkv, ldo;
   bool causal;
 };
 hipError_t launch_attention(const AttnDesc& a, hipStream_t s);

@@ -1,0 +1,189 @@
+"""GPU parity of the head-sharded attention path (QKV column GEMMs by head + causal
+attention core), the row-sharded output projection, and the full TP block of the
+GPT-style workload, against the CPU oracle, through the C ABI."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _gpu_util import BF16_TOL, dev, f64, host64, log, nerr, requires_gpu, sample_rows
+from megatron_tensor_transformer_gemm_amd import inputs as I
+from megatron_tensor_transformer_gemm_amd import tpshard as S
+from oracle import tp_oracle as O
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+BF = S.TP_BF16
+
+
+def _heads(xd, wqd, wkd, wvd, n_seq, seq_len, d, H, KV, dh, T_p, t, causal):
+    h_t = H // T_p
+    T = n_seq * seq_len
+    o = torch.full((T, h_t * dh), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    nb = S.tp_attn_heads_workspace_bytes(n_seq, seq_len, H, KV, dh, T_p)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda:0")
+    S.tp_attn_heads_shard_fwd(xd, wqd, wkd, wvd, o, ws, ws.numel(), n_seq, seq_len, d, H, KV, dh,
+                              T_p, t, causal)
+    torch.cuda.synchronize()
+    return o
+
+
+def _rand_bf16(shape, seed, std):
+    return I.bf16_bits(np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * std)
+
+
+CASES = [
+    # n_seq, seq_len, d, H, KV, dh, T_p, causal
+    (2, 200, 256, 8, 4, 64, 2, True),
+    (1, 333, 256, 4, 4, 128, 2, True),
+    (3, 64, 128, 4, 2, 128, 1, True),
+    (1, 130, 192, 8, 8, 128, 4, False),
+    (2, 1, 64, 2, 2, 64, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}x{c[1]}-d{c[2]}-H{c[3]}-KV{c[4]}-dh{c[5]}-tp{c[6]}-"
+                                             f"{'causal' if c[7] else 'full'}" for c in CASES])
+def test_attention_heads_parity(case):
+    n_seq, L, d, H, KV, dh, T_p, causal = case
+    log(f"[attn] {case}")
+    T = n_seq * L
+    x = _rand_bf16((T, d), 1, 1.0)
+    wq = _rand_bf16((d, H * dh), 2, 1 / math.sqrt(d))
+    wk = _rand_bf16((d, KV * dh), 3, 1 / math.sqrt(d))
+    wv = _rand_bf16((d, KV * dh), 4, 1 / math.sqrt(d))
+    xd, wqd, wkd, wvd = (dev(a, I.BF16) for a in (x, wq, wk, wv))
+    x64, wq64, wk64, wv64 = (f64(a, I.BF16) for a in (x, wq, wk, wv))
+    for t in range(T_p):
+        o = host64(_heads(xd, wqd, wkd, wvd, n_seq, L, d, H, KV, dh, T_p, t, causal))
+        ref = np.concatenate([O.attn_heads_shard(x64[s * L:(s + 1) * L], wq64, wk64, wv64, H, KV, dh,
+                                                 T_p, t, causal=causal) for s in range(n_seq)])
+        e = nerr(o, ref)
+        log(f"   t={t} err(O)={e:.3e}")
+        assert e <= BF16_TOL
+
+
+def test_attention_zero_queries_give_prefix_means():
+    """Wq = 0 makes every score 0: causal attention then averages V over keys 0..i."""
+    L, d, H, dh = 96, 128, 2, 64
+    x = _rand_bf16((L, d), 5, 1.0)
+    wq = np.zeros((d, H * dh), dtype=np.uint16)
+    wk = _rand_bf16((d, H * dh), 6, 0.1)
+    wv = _rand_bf16((d, H * dh), 7, 0.1)
+    o = host64(_heads(*(dev(a, I.BF16) for a in (x, wq, wk, wv)), 1, L, d, H, H, dh, 1, 0, True))
+    v = f64(x, I.BF16) @ f64(wv, I.BF16)
+    ref = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None]
+    assert nerr(o, ref) <= BF16_TOL
+    # row 0 sees only key 0
+    assert nerr(o[0], v[0]) <= BF16_TOL
+
+
+def test_outproj_parity_small_and_gqa():
+    T, d, H, KV, dh, T_p = 300, 264, 16, 4, 64, 4
+    kdim = H // T_p * dh
+    wo = _rand_bf16((H * dh, d), 8, 1 / math.sqrt(H * dh))
+    wod = dev(wo, I.BF16)
+    parts = torch.empty((T_p, T, d), dtype=torch.bfloat16, device="cuda:0")
+    o_full = _rand_bf16((T, H * dh), 9, 1.0)
+    for t in range(T_p):
+        o_t = dev(np.ascontiguousarray(o_full[:, t * kdim:(t + 1) * kdim]), I.BF16)
+        S.tp_attn_outproj_shard_fwd(o_t, wod, parts[t], T, d, H, KV, dh, T_p, t, BF, BF)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_partial_sum(parts, T * d, T_p, None, y, T * d, BF, BF)
+    torch.cuda.synchronize()
+    for t in range(T_p):
+        ref = O.attn_outproj_shard(f64(o_full[:, t * kdim:(t + 1) * kdim], I.BF16), f64(wo, I.BF16),
+                                   H, KV, dh, T_p, t)
+        assert nerr(host64(parts[t]), ref) <= BF16_TOL
+    assert nerr(host64(y), f64(o_full, I.BF16) @ f64(wo, I.BF16)) <= BF16_TOL
+
+
+def test_outproj_workload_sampled():
+    """Llama-3-70B-shaped out-projection: 64 query / 8 KV heads of 128, 8 per rank."""
+    w = I.WORKLOADS[4]
+    T_p = w.T_p
+    kdim = w.n_heads // T_p * w.head_dim
+    o_full = I.make_tensor(w, "o")
+    wo = I.make_tensor(w, "wo")
+    wod = dev(wo, I.BF16)
+    rows = sample_rows(w.T, 254, seed=41)
+    parts = torch.empty((T_p, w.T, w.d), dtype=torch.bfloat16, device="cuda:0")
+    refs = []
+    for t in range(T_p):
+        o_t = dev(np.ascontiguousarray(o_full[:, t * kdim:(t + 1) * kdim]), I.BF16)
+        S.tp_attn_outproj_shard_fwd(o_t, wod, parts[t], w.T, w.d, w.n_heads, w.n_kv_heads,
+                                    w.head_dim, T_p, t, BF, BF)
+        torch.cuda.synchronize()
+        ref = O.attn_outproj_shard(f64(o_full[rows, t * kdim:(t + 1) * kdim], I.BF16),
+                                   I.bf16_to_f32(wo), w.n_heads, w.n_kv_heads, w.head_dim, T_p, t)
+        e = nerr(host64(parts[t][rows]), ref)
+        log(f"   t={t} err(a)={e:.3e}")
+        assert e <= BF16_TOL
+        refs.append(ref)
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_partial_sum(parts, w.T * w.d, T_p, None, y, w.T * w.d, BF, BF)
+    torch.cuda.synchronize()
+    assert nerr(host64(y[rows]), O.partial_sum(refs)) <= BF16_TOL
+
+
+def run_block_sequence(w, dv, x_s, T_p):
+    """One sequence through all T_p ranks of the block on the GPU: returns (x1, y)."""
+    L, d = x_s.shape
+    H, KV, dh = w.n_heads, w.n_kv_heads, w.head_dim
+    kdim = H // T_p * dh
+    parts = torch.empty((T_p, L, d), dtype=torch.bfloat16, device="cuda:0")
+    o_t = torch.empty((L, kdim), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(S.tp_attn_heads_workspace_bytes(1, L, H, KV, dh, T_p), dtype=torch.uint8,
+                     device="cuda:0")
+    for t in range(T_p):
+        S.tp_attn_heads_shard_fwd(x_s, dv["wq"], dv["wk"], dv["wv"], o_t, ws, ws.numel(), 1, L, d,
+                                  H, KV, dh, T_p, t, True)
+        S.tp_attn_outproj_shard_fwd(o_t, dv["wo"], parts[t], L, d, H, KV, dh, T_p, t, BF, BF)
+    x1 = torch.empty((L, d), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_partial_sum(parts, L * d, T_p, x_s, x1, L * d, BF, BF)
+    h = torch.empty(S.tp_ffn_workspace_bytes(L, w.d_ff, T_p, BF), dtype=torch.uint8, device="cuda:0")
+    for t in range(T_p):
+        S.tp_ffn_shard_fwd(x1, dv["w1"], None, dv["w2"], parts[t], h, h.numel(), L, d, w.d_ff, T_p,
+                           t, "gelu", BF, BF)
+    y = torch.empty((L, d), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_partial_sum(parts, L * d, T_p, x1, y, L * d, BF, BF)
+    return x1, y
+
+
+@pytest.mark.slow
+def test_gpt_block_workload_sampled():
+    """GPT-style d=6144 TP8 block: 4 micro-batches of one 2048-token sequence run back to
+    back through every rank's attention and FFN shards with the two local reduces; the
+    oracle checks sampled token rows of the first and last micro-batch."""
+    w = I.WORKLOADS[5]
+    log(f"[block] {w.name}: generating inputs")
+    host = {k: I.make_tensor(w, k) for k in ("x", "wq", "wk", "wv", "wo", "w1", "w2")}
+    dv = {k: dev(v, I.BF16) for k, v in host.items() if k != "x"}
+    xd = dev(host["x"], I.BF16)
+    W64 = {k: I.bf16_to_f32(v) for k, v in host.items() if k != "x"}
+    L = w.seq_len
+    outs = []
+    for s in range(w.n_seq):
+        outs.append(run_block_sequence(w, dv, xd[s * L:(s + 1) * L], w.T_p))
+    torch.cuda.synchronize()
+    for s in (0, w.n_seq - 1):
+        rows = sample_rows(L, 126, seed=50 + s)
+        x_s = f64(host["x"][s * L:(s + 1) * L], I.BF16)
+        x1_ref, y_ref = O.block_sequence(x_s, W64, w.n_heads, w.n_kv_heads, w.head_dim, w.T_p,
+                                         act="gelu", rows=rows)
+        e1 = nerr(host64(outs[s][0][rows]), x1_ref)
+        e2 = nerr(host64(outs[s][1][rows]), y_ref)
+        log(f"   micro-batch {s}: err(x1)={e1:.3e} err(y)={e2:.3e}")
+        assert e1 <= BF16_TOL and e2 <= BF16_TOL
+
+
+def test_attention_gqa_divisibility_rejected():
+    x = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda:0")
+    w = torch.zeros((128, 64 * 128), dtype=torch.bfloat16, device="cuda:0")
+    o = torch.zeros((64, 4 * 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_heads_shard_fwd(x, w, w, w, o, o, o.numel() * 2, 1, 64, 128, 64, 8, 128, 16, 0,
+                                  True)
+    assert e.value.code == S.TP_ERR_NOT_DIVISIBLE
