@@ -72,7 +72,16 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="read the rocprofv3 counter_collection.csv files of two --pmc-pass "
+                         "runs (FETCH_SIZE, WRITE_SIZE), write profiles/hbm_traffic.json, exit")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run each kernel of one step once, then a plain 1 GiB device copy "
+                         "(the calibration for the HBM byte counters), and exit")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        return ingest_pmc(*args.ingest_pmc)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -151,6 +160,23 @@ def main() -> int:
             k += 1
             evs[k].record()
 
+    if args.pmc_pass:
+        # one launch of each kernel class, then a copy of known size
+        S.tp_ffn_column_fwd(X, W1, W3, H, T, d, d_ff, T_p, 0, S.TP_ACT_SWIGLU, BF)
+        S.tp_ffn_row_fwd(H, W2, P[0], T, d, d_ff, T_p, 0, BF, BF)
+        S.tp_partial_sum(P, T * d, T_p, None, Y, T * d, BF, BF)
+        S.tp_attn_outproj_shard_fwd(O_t[0], WO, P[0], T, d, w.n_heads, w.n_kv_heads, w.head_dim,
+                                    T_p, 0, BF, BF)
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] pmc pass done: column GEMM, row GEMM, partial sum, out-projection, "
+            "1 GiB copy")
+        return 0
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -228,6 +254,47 @@ def main() -> int:
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    return 0
+
+
+PMC_PASS_KERNELS = ["column_gemm_swiglu", "row_gemm", "partial_sum", "attn_outproj_gemm"]
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
+    """Per-launch HBM bytes of each kernel of the --pmc-pass run.
+
+    FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by
+    (bytes a plain 1 GiB copy really moves) / (what the same counter reads for that copy).
+    Dispatch order of --pmc-pass: column GEMM, row GEMM, partial sum, out-projection,
+    fill, copy."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    f_copy = [v for n, v in fetch if "copy" in n.lower()][-1] * 1024.0
+    w_copy = [v for n, v in write if "copy" in n.lower()][-1] * 1024.0
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    out = {"workload": "llama3_70b_swiglu_bf16", "source_digest": kernel_source_digest(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_counted": f_copy,
+                           "write_counted": w_copy, "fetch_scale": f_scale,
+                           "write_scale": w_scale},
+           "kernels": {}}
+    for i, name in enumerate(PMC_PASS_KERNELS):
+        fb = fetch[i][1] * 1024.0 * f_scale
+        wb = write[i][1] * 1024.0 * w_scale
+        out["kernels"][f"{name}@llama3_70b_swiglu_bf16"] = {
+            "kernel_symbol": fetch[i][0], "fetch_bytes": fb, "write_bytes": wb,
+            "bytes_per_launch": fb + wb, "source_digest": out["source_digest"]}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out["kernels"], indent=1))
     return 0
 
 
