@@ -268,7 +268,7 @@ def test_pages_printed_values(row):
         assert abs(float(got) - float(printed)) <= float(tol) + 1e-12, (name, float(got))
 
 
-def test_bubble_north_star_value():
+def test_bubble_four_stages_eight_micro_batches():
     assert analytic.bubble_fraction(4, 8) == Fraction(3, 11)
     # the two normalisations describe the same idle time
     assert analytic.bubble_vs_useful(4, 8) * 8 == analytic.bubble_fraction(4, 8) * 11
