@@ -42,7 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;          // k per LDS stage
 constexpr int kThreads = 256;    // 4 waves
 constexpr uint32_t kOOB = 0x40000000u;       // voffset of a masked lane: >= num_records
 constexpr int kNumRecords = 0x40000000;      // every valid per-lane offset is below 1 GiB
@@ -53,10 +52,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                            kRsrcWord3);
 }
 
-// Physical 16-byte chunk (of 8 per 128-byte A row) holding logical chunk c of row r is
-// c ^ swz_a(r): 16 consecutive rows read at the same logical chunk land on 16 distinct
-// 4-bank groups (and 8 consecutive rows on 8 distinct groups).
-__device__ __forceinline__ int swz_a(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor as four SGPRs, for the copy below.
+__device__ __forceinline__ i32x4 make_desc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xFFFF, kNumRecords, kRsrcWord3};
+}
+
+// One buffer_load_dwordx4 ... lds: each lane copies 16 bytes from desc+voff into
+// LDS at lds_base + 16*lane.  Issued as inline assembly so that the compiler does not
+// track the asynchronous LDS write: completion is managed explicitly (vmcnt + barrier),
+// which lets several stages stay in flight.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved, yet this asm does set it
+__device__ __forceinline__ void copy16_to_lds(const i32x4& desc, uint32_t voff,
+                                              uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(desc), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Physical chunk of logical chunk c in B k-row r is c ^ swz_b(r): the four k-rows a
 // transposing read touches at once get disjoint chunk sets both in 32-byte pairs and in
@@ -91,7 +111,28 @@ __device__ __forceinline__ float epilogue(float u, float v) {
   else return u;
 }
 
-template <int BM, int BN, bool DUAL, int ACT, bool OUT_F32>
+// Physical chunk of logical chunk c in A row r (ACPR 16-byte chunks per row) is
+// c ^ swz_a<ACPR>(r): 16 consecutive rows read at one logical chunk land on 16 distinct
+// 4-bank groups, and 8 consecutive rows on 8 distinct groups.
+template <int ACPR>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (ACPR == 8) return (r ^ ((r >> 3) & 3)) & 7;
+  else return ((r >> 2) ^ (r >> 1)) & 3;
+}
+
+// Workgroup barrier after this wave's copies have landed except for the newest I, and
+// its LDS reads have completed.  (A __syncthreads() would also wait for every copy in
+// flight: the fence it carries treats them as pending stores.)
+template <int I>
+__device__ __forceinline__ void sync_copies() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(I) : "memory");
+}
+
+// BK k per LDS stage, NST stages in flight.  The stage boundary is moved one 16-k substep
+// early: the wait and barrier for stage k+1 happen before the last substep of stage k, so
+// the next stage's first fragments are read, and the copies of stage k+NST are issued into
+// stage k's (now free) buffer, while that last substep multiplies.
+template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int tiles_m, int tiles_n) {
   constexpr int NSUB = DUAL ? 2 : 1;          // B sub-tiles: W1 block | W3 block
   constexpr int BNS = BN / NSUB;              // B columns per sub-tile = output tile width
@@ -100,22 +141,40 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   constexpr int WCOLS = BNS / 2;              // sub-tile columns per wave
   constexpr int NBS = WCOLS / 32;             // 32-column MFMA blocks per wave per sub-tile
   constexpr int NB = NBS * NSUB;
-  constexpr int A_BYTES = BM * kBK * 2;
-  constexpr int SUB_BYTES = kBK * BNS * 2;
+  constexpr int KSUB = BK / 16;               // 16-k substeps per stage
+  constexpr int ACPR = BK / 8;                // 16-byte chunks per A row
+  constexpr int AROWB = BK * 2;               // bytes per A row
+  constexpr int ARPI = 1024 / AROWB;          // A rows per 1 KiB copy
+  constexpr int A_BYTES = BM * AROWB;
+  constexpr int SUB_BYTES = BK * BNS * 2;
   constexpr int STAGE = A_BYTES + NSUB * SUB_BYTES;
-  constexpr int A_LD = A_BYTES / 1024 / 4;    // 1 KiB buffer->LDS loads per wave per stage
+  constexpr int A_LD = A_BYTES / 1024 / 4;    // 1 KiB buffer->LDS copies per wave per stage
   constexpr int B_LD = NSUB * SUB_BYTES / 1024 / 4;
-  constexpr int QSUB = SUB_BYTES / 1024;      // loads per sub-tile
+  constexpr int LPS = A_LD + B_LD;            // copies per wave per stage
+  constexpr int QSUB = SUB_BYTES / 1024;      // copies per sub-tile
   constexpr int CPR = BNS / 8;                // 16-byte chunks per B row
   constexpr int PITCH = BNS * 2;              // bytes per B row
   static_assert(MB >= 1 && NBS >= 1 && A_LD >= 1 && B_LD >= 1, "tile too small");
   static_assert(CPR >= 8, "B sub-tile narrower than 64 columns");
+  static_assert(KSUB % 2 == 0 && (ACPR == 4 || ACPR == 8), "BK must be 32 or 64");
+  static_assert(NST >= 2 && NST <= 5 && (NST - 1) * LPS <= 63, "stages");
 
-  // One array per stage: the buffer->LDS copies into one stage and the fragment reads
-  // of the other are then provably disjoint, so no wait on the copies is inserted
-  // before the reads (the copies of stage k+1 overlap the products of stage k).
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[STAGE];
+  // One array per stage: copies into one stage and fragment reads of another are then
+  // provably disjoint, so the compiler inserts no wait on the copies before the reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[NST > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[NST > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char st4[NST > 4 ? STAGE : 16];
+  auto buf = [&](int i) -> LDS_AS unsigned char* {
+    switch (i) {
+      case 0: return (LDS_AS unsigned char*)st0;
+      case 1: return (LDS_AS unsigned char*)st1;
+      case 2: return (LDS_AS unsigned char*)st2;
+      case 3: return (LDS_AS unsigned char*)st3;
+      default: return (LDS_AS unsigned char*)st4;
+    }
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,8 +198,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = wave * A_LD + i;
-    const int row = q * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_a(row);
+    const int row = q * ARPI + lane / ACPR;
+    const int c = (lane % ACPR) ^ swz_a<ACPR>(row);
     a_voff[i] = row < rows_left ? (uint32_t)(row * g.lda + 8 * c) * 2u : kOOB;
     a_kc[i] = 8 * c;
   }
@@ -158,51 +217,32 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // B sub-tile a wave's copies land in is the same for all of its copies.
   const bool b_second = (wave * B_LD) / QSUB != 0;
 
-  // (Each offset goes through a local before the builtin call: handing the builtin an
-  // element of a captured array directly makes the host compilation pass drop the
-  // kernel's launch stub.)
   auto issue = [&](int kt, LDS_AS unsigned char* base) {
-    const int k0 = kt * kBK;
-    const bool full = k0 + kBK <= g.K;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + k0);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc((b_second ? B1 : B0) + (int64_t)k0 * g.ldb);
-    if (full) {
+    const int k0 = kt * BK;
+    const bool full = k0 + BK <= g.K;
+    const i32x4 da = make_desc(A + k0);
+    const i32x4 db = make_desc((b_second ? B1 : B0) + (int64_t)k0 * g.ldb);
+    const uint32_t lds = (uint32_t)(uintptr_t)base;
 #pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const uint32_t v = a_voff[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (LDS_AS void*)(base + (wave * A_LD + i) * 1024), 16, v, 0, 0, 0);
-      }
+    for (int i = 0; i < A_LD; ++i) {
+      const uint32_t v = (full || k0 + a_kc[i] < g.K) ? a_voff[i] : kOOB;
+      copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (wave * A_LD + i) * 1024));
+    }
 #pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        const uint32_t v = b_voff[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (LDS_AS void*)(base + A_BYTES + (wave * B_LD + i) * 1024), 16, v, 0, 0, 0);
-      }
-    } else {  // last, partial k-tile
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const uint32_t v = (k0 + a_kc[i] < g.K) ? a_voff[i] : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (LDS_AS void*)(base + (wave * A_LD + i) * 1024), 16, v, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        const uint32_t v = (k0 + b_kr[i] < g.K) ? b_voff[i] : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (LDS_AS void*)(base + A_BYTES + (wave * B_LD + i) * 1024), 16, v, 0, 0, 0);
-      }
+    for (int i = 0; i < B_LD; ++i) {
+      const uint32_t v = (full || k0 + b_kr[i] < g.K) ? b_voff[i] : kOOB;
+      copy16_to_lds(db, v,
+                    __builtin_amdgcn_readfirstlane(lds + A_BYTES + (wave * B_LD + i) * 1024));
     }
   };
 
-
   // ---- per-lane LDS read offsets
   const int arow = wm * WTM + (lane & 31);
-  uint32_t a_rd[4];
+  uint32_t a_rd[KSUB];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < KSUB; ++s) {
     const int c = 2 * s + (lane >> 5);
-    a_rd[s] = (uint32_t)(arow * 128 + ((c ^ swz_a(arow)) << 4));
+    a_rd[s] = (uint32_t)(arow * AROWB + ((c ^ swz_a<ACPR>(arow)) << 4));
   }
   const int g4 = lane >> 4, i16 = lane & 15;
   const int krow_l = 8 * (g4 >> 1) + (i16 >> 2);
@@ -229,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
     const LDS_AS unsigned char* Bs = As + A_BYTES;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * 128);
+      af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * AROWB);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
@@ -238,67 +278,69 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
-  // All products of one stage.  The fragments of substep s+1 are read while substep s
-  // multiplies: the scheduler is told to alternate one MFMA with one LDS read.
+  auto mfmas = [&](const bf16x8 (&af)[MB], const bf16x8 (&bfr)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[mb][nb], 0, 0, 0);
+  };
+  // Scheduling hint for one substep with the next substep's reads: alternate one MFMA and
+  // one LDS read, then the rest.
   constexpr int NREAD = MB + 2 * NB;  // LDS reads per substep
   constexpr int NMFMA = MB * NB;      // MFMAs per substep
   constexpr int NPAIR = NMFMA < NREAD ? NMFMA : NREAD;
-  auto compute = [&](const LDS_AS unsigned char* As) {
-    bf16x8 af[2][MB];
-    bf16x8 bfr[2][NB];
-    load_frags(As, 0, af[0], bfr[0]);
+  auto interleave = [&]() {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) load_frags(As, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][nb], af[s & 1][mb],
-                                                                 acc[mb][nb], 0, 0, 0);
+    for (int i = 0; i < NPAIR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // schedule: reads of substep 0, then per substep one MFMA / one read pairs
-    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-#pragma unroll
-        for (int i = 0; i < NPAIR; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
-        if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
-      }
-    }
+    if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
+    if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
   };
 
-  LDS_AS unsigned char* S0 = (LDS_AS unsigned char*)smem0;
-  LDS_AS unsigned char* S1 = (LDS_AS unsigned char*)smem1;
-  const int nk = (g.K + kBK - 1) / kBK;
-  issue(0, S0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue(kt + 1, S1);                        // stays ahead of the products below
+  bf16x8 af[2][MB];
+  bf16x8 bfr[2][NB];
+  // k-tiles, padded to a multiple of NST: tiles past K load as zeros (every copy
+  // out of range), so every stage runs the same branch-free product code.
+  const int nk = ((g.K + BK - 1) / BK + NST - 1) / NST * NST;
+
+  // prologue: NST stages in flight, then stage 0's first fragments
+#pragma unroll
+  for (int p = 0; p < NST; ++p) issue(p, buf(p));
+  sync_copies<(NST - 1) * LPS>();
+  load_frags(buf(0), 0, af[0], bfr[0]);
+
+  // One stage; `u` is the stage's buffer (kt mod NST), a constant after unrolling.
+  auto stage = [&](int kt, int u) {
+    LDS_AS unsigned char* cur = buf(u);
+    LDS_AS unsigned char* nxt = buf(u + 1 == NST ? 0 : u + 1);
+#pragma unroll
+    for (int s = 0; s + 1 < KSUB; ++s) {
+      load_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+      mfmas(af[s & 1], bfr[s & 1]);
+      interleave();
+    }
     __builtin_amdgcn_sched_barrier(0);
-    compute(S0);
+    // Stage kt+1 is complete for every wave; stage kt's buffer is free for stage kt+NST.
+    // Past the end the copies are all out of range (zero fill, no memory traffic), so
+    // every stage issues the same number of copies and the loop has no branches.
+    sync_copies<(NST - 2) * LPS>();
+    issue(kt + NST, cur);
+    // (after the last stage this reads a stale buffer; the fragments are not used)
+    load_frags(nxt, 0, af[0], bfr[0]);
+    mfmas(af[1], bfr[1]);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) issue(kt + 2, S0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(S1);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  for (int kt0 = 0; kt0 < nk; kt0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) stage(kt0 + u, u);
   }
-  if (kt < nk) {  // odd number of k-tiles: the last one sits in stage 0
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute(S0);
-  }
+  // the trailing zero-fill copies must land before this workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: activation on the fp32 accumulators, one rounding, vector stores
 #pragma unroll
@@ -331,24 +373,29 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   }
 }
 
-template <int BM, int BN, bool DUAL, int ACT, bool OUT_F32>
+template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32>
 hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? BN / 2 : BN;
   const int64_t tm = (g.M + BM - 1) / BM;
   const int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, DUAL, ACT, OUT_F32>), dim3((unsigned)(tm * tn)),
-                     dim3(kThreads), 0, s, g, (int)tm, (int)tn);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, DUAL, ACT, OUT_F32>),
+                     dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
 
-// Large tiles once they give at least one full wave of workgroups over the 256 CUs.
+// Tile choice: 256x256 tiles once they give at least one full wave of workgroups over the
+// 256 CUs, else 128x128 (or 128x256 for the gated pair).  Long k-loops use 4 stages of 32 k
+// (more copies in flight); short ones 2 stages of 64 k (fewer, longer stages).
 template <bool DUAL, int ACT, bool OUT_F32>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
   const int64_t big = ((g.M + 255) / 256) * ((g.N + OUT_BN - 1) / OUT_BN);
-  if (big >= 256) return launch_cfg<256, 256, DUAL, ACT, OUT_F32>(g, s);
-  return launch_cfg<128, DUAL ? 256 : 128, DUAL, ACT, OUT_F32>(g, s);
+  if (big >= 256) {
+    if (g.K > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32>(g, s);
+    return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32>(g, s);
+  }
+  return launch_cfg<128, DUAL ? 256 : 128, 64, 2, DUAL, ACT, OUT_F32>(g, s);
 }
 
 }  // namespace
