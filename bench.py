@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TOL = 2e-2                    # normwise max relative error, bf16 with fp32 accumulation
+PSUM_PAD = 2048               # elements between partial slices (4 KiB of bf16)
 
 
 def log(msg: str) -> None:
@@ -72,6 +73,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="token rows of the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the extra GPT-style block measurement (attention core)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="read the rocprofv3 counter_collection.csv files of two --pmc-pass "
                          "runs (FETCH_SIZE, WRITE_SIZE), write profiles/hbm_traffic.json, exit")
@@ -118,7 +121,12 @@ def main() -> int:
     X, W1, W3, W2, WO = (dev(host[k]) for k in ("x", "w1", "w3", "w2", "wo"))
     O_t = [dev(host["o"][:, t * kdim:(t + 1) * kdim]) for t in range(T_p)]
     H = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
-    P = torch.empty((T_p, T, d), dtype=torch.bfloat16, device="cuda")
+    # Partial buffer: slice t holds y(t) [T, d]; the slices are padded by 4 KiB so that the
+    # same element of every slice does not fall on the same DRAM banks (the slice size,
+    # 2^28 bytes here, is a power of two).
+    stride = T * d + PSUM_PAD
+    P_flat = torch.empty(T_p * stride, dtype=torch.bfloat16, device="cuda")
+    P = [P_flat[t * stride: t * stride + T * d].view(T, d) for t in range(T_p)]
     Y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     A = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
@@ -145,7 +153,7 @@ def main() -> int:
             if evs:
                 k += 1
                 evs[k].record()
-        S.tp_partial_sum(P, T * d, T_p, None, Y, T * d, BF, BF)
+        S.tp_partial_sum(P_flat, stride, T_p, None, Y, T * d, BF, BF)
         if evs:
             k += 1
             evs[k].record()
@@ -155,7 +163,7 @@ def main() -> int:
             if evs:
                 k += 1
                 evs[k].record()
-        S.tp_partial_sum(P, T * d, T_p, None, A, T * d, BF, BF)
+        S.tp_partial_sum(P_flat, stride, T_p, None, A, T * d, BF, BF)
         if evs:
             k += 1
             evs[k].record()
@@ -164,7 +172,7 @@ def main() -> int:
         # one launch of each kernel class, then a copy of known size
         S.tp_ffn_column_fwd(X, W1, W3, H, T, d, d_ff, T_p, 0, S.TP_ACT_SWIGLU, BF)
         S.tp_ffn_row_fwd(H, W2, P[0], T, d, d_ff, T_p, 0, BF, BF)
-        S.tp_partial_sum(P, T * d, T_p, None, Y, T * d, BF, BF)
+        S.tp_partial_sum(P_flat, stride, T_p, None, Y, T * d, BF, BF)
         S.tp_attn_outproj_shard_fwd(O_t[0], WO, P[0], T, d, w.n_heads, w.n_kv_heads, w.head_dim,
                                     T_p, 0, BF, BF)
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
@@ -249,6 +257,8 @@ def main() -> int:
         "roofline": roofline,
     }
 
+    if not args.no_block:
+        out["block_workload"] = measure_block(max(2, args.steps // 4), 1)
     if not args.no_cpu_baseline:
         out.update(cpu_baseline(host, w, Y, A, args.cpu_rows))
     else:
@@ -296,6 +306,128 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
         json.dump(out, f, indent=1)
     print(json.dumps(out["kernels"], indent=1))
     return 0
+
+
+def measure_block(steps: int, warmup: int) -> dict:
+    """GPT-style TP8 block (d=6144, 48 heads of 128, d_ff=24576, GELU), 4 micro-batches of one
+    2048-token sequence, all ranks: per rank QKV projections + causal attention core +
+    out-projection, reduce with residual, per rank column + row GEMM, reduce with residual.
+    Reports the block's GEMM+attention FLOP rate and per-kernel times, including the
+    attention core alone (causal FLOPs 2*h_t*d_h*L*(L+1) per rank and sequence)."""
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from megatron_tensor_transformer_gemm_amd import tpshard as S
+
+    torch.cuda.empty_cache()
+    w = I.WORKLOADS[5]
+    T_p, d, L, H, dh = w.T_p, w.d, w.seq_len, w.n_heads, w.head_dim
+    h_t = H // T_p
+    n = w.d_ff // T_p
+    kdim = h_t * dh
+    BF = S.TP_BF16
+    log(f"[bench] block workload {w.name}: generating inputs")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    Wd = {k: dev(I.make_tensor(w, k)) for k in ("wq", "wk", "wv", "wo", "w1", "w2")}
+    X = dev(I.make_tensor(w, "x"))
+    stride = L * d + PSUM_PAD
+    Pf = torch.empty(T_p * stride, dtype=torch.bfloat16, device="cuda")
+    P = [Pf[t * stride: t * stride + L * d].view(L, d) for t in range(T_p)]
+    o_t = torch.empty((L, kdim), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(S.tp_attn_heads_workspace_bytes(1, L, H, H, dh, T_p), dtype=torch.uint8,
+                     device="cuda")
+    Hh = torch.empty((L, n), dtype=torch.bfloat16, device="cuda")
+    x1 = torch.empty((L, d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((w.T, d), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    names = []
+    for _ in range(w.n_seq):
+        names += ["attn_heads", "outproj"] * T_p + ["psum"] + ["col", "row"] * T_p + ["psum"]
+
+    def step(evs=None):
+        k = [0]
+
+        def mark():
+            if evs:
+                k[0] += 1
+                evs[k[0]].record()
+        if evs:
+            evs[0].record()
+        for s_ in range(w.n_seq):
+            xs = X[s_ * L:(s_ + 1) * L]
+            for t in range(T_p):
+                S.tp_attn_heads_shard_fwd(xs, Wd["wq"], Wd["wk"], Wd["wv"], o_t, ws, ws.numel(), 1, L,
+                                          d, H, H, dh, T_p, t, True)
+                mark()
+                S.tp_attn_outproj_shard_fwd(o_t, Wd["wo"], P[t], L, d, H, H, dh, T_p, t, BF, BF)
+                mark()
+            S.tp_partial_sum(Pf, stride, T_p, xs, x1, L * d, BF, BF)
+            mark()
+            for t in range(T_p):
+                S.tp_ffn_column_fwd(x1, Wd["w1"], None, Hh, L, d, w.d_ff, T_p, t, S.TP_ACT_GELU, BF)
+                mark()
+                S.tp_ffn_row_fwd(Hh, Wd["w2"], P[t], L, d, w.d_ff, T_p, t, BF, BF)
+                mark()
+            S.tp_partial_sum(Pf, stride, T_p, x1, y[s_ * L:(s_ + 1) * L], L * d, BF, BF)
+            mark()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    dur = {}
+    for s_ in range(steps):
+        for i, nm in enumerate(names):
+            dur.setdefault(nm, []).append(ev[s_][i].elapsed_time(ev[s_][i + 1]))
+    avg = {k: 1e3 * sum(v) / len(v) for k, v in dur.items()}
+    # the attention core alone, on the last rank's projected heads
+    q = ws.view(torch.bfloat16)
+    qv = q[: L * kdim]
+    kv = q[L * kdim: 2 * L * kdim]
+    vv = q[2 * L * kdim: 3 * L * kdim]
+    for _ in range(3):
+        S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
+    e1.record()
+    torch.cuda.synchronize()
+    core_us = e0.elapsed_time(e1) * 1e3 / 20
+    fl_qkv = 2.0 * L * d * 3 * kdim
+    fl_core = 2.0 * h_t * dh * L * (L + 1)
+    fl_out = 2.0 * L * kdim * d
+    fl_ffn1 = 2.0 * L * d * n
+    fl_ffn2 = 2.0 * L * n * d
+    fl_step = w.n_seq * T_p * (fl_qkv + fl_core + fl_out + fl_ffn1 + fl_ffn2)
+
+    def tf(fl, us):
+        return round(fl / (us * 1e-6) / 1e12, 1)
+    res = {
+        "workload": w.name, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "tflops": round(fl_step / (ms * 1e-3) / 1e12, 2), "step_flops": fl_step,
+        "kernels": {
+            "qkv_projection_plus_attention_core": {"avg_us": round(avg["attn_heads"], 2),
+                                                   "tflops": tf(fl_qkv + fl_core, avg["attn_heads"])},
+            "attention_core_causal": {"avg_us": round(core_us, 2), "tflops": tf(fl_core, core_us),
+                                      "frac_peak": round(fl_core / (core_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "attn_outproj_gemm": {"avg_us": round(avg["outproj"], 2), "tflops": tf(fl_out, avg["outproj"])},
+            "column_gemm_gelu": {"avg_us": round(avg["col"], 2), "tflops": tf(fl_ffn1, avg["col"])},
+            "row_gemm": {"avg_us": round(avg["row"], 2), "tflops": tf(fl_ffn2, avg["row"])},
+            "partial_sum_residual": {"avg_us": round(avg["psum"], 2)},
+        },
+    }
+    log(f"[bench] block: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; attention core {core_us:.1f} us")
+    return res
 
 
 def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:

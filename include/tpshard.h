@@ -185,6 +185,22 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
                             int32_t T_p, int32_t t, int32_t causal, void* hip_stream);
 
 /*
+ * The attention core alone (the second half of tp_attn_heads_shard_fwd), on the rank's
+ * already-projected heads: for each local query head j and sequence s,
+ *     O_j = softmax(Q_j K_kv(j)^T / sqrt(head_dim) [+ causal mask]) V_kv(j),
+ * kv(j) = j / (h_t / kv_t).  bf16 in and out, fp32 softmax statistics.
+ *
+ *   q      [n_seq*seq_len, ldq]   head j in columns [j*head_dim, (j+1)*head_dim), ldq >= h_t*head_dim
+ *   k, v   [n_seq*seq_len, ldkv]  KV head i in columns [i*head_dim, ...), ldkv >= kv_t*head_dim
+ *   o      [n_seq*seq_len, ldo]   written like q
+ * h_t % kv_t must be 0; head_dim 64 or 128; leading dimensions multiples of 8.
+ */
+int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o,
+                     int64_t n_seq, int64_t seq_len, int32_t h_t, int32_t kv_t,
+                     int32_t head_dim, int64_t ldq, int64_t ldkv, int64_t ldo,
+                     int32_t causal, void* hip_stream);
+
+/*
  * Local partial sum standing in for the all-reduce ("7.9 Tensor and
  * pipeline parallelism", section 2.1: y is the sum over ranks of y(t)):
  *     y[i] = sum_{t=0}^{T_p-1} partials[t*partial_stride + i]  (+ residual[i])
@@ -192,7 +208,10 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
  * out_dtype.  The order is fixed, so repeated calls are bitwise identical.
  *
  *   partials        T_p slices of n_elems elements, part_dtype, slice t at
- *                   offset t*partial_stride elements (partial_stride >= n_elems)
+ *                   offset t*partial_stride elements (partial_stride >= n_elems,
+ *                   a multiple of 8 when T_p > 1).  A stride that is a large power
+ *                   of two maps the same element of every slice onto the same DRAM
+ *                   banks; padding it by a few KiB streams measurably faster.
  *   residual        NULL or [n_elems] out_dtype; may equal y (in place)
  *   y               [n_elems] out_dtype; must not overlap the partials
  * Supported: part_dtype and out_dtype each BF16 or F32.  n_elems == 0 is a no-op.

@@ -348,6 +348,46 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
   return hip_status(tpk::launch_attention(a, s), "attention launch");
 }
 
+int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64_t n_seq,
+                     int64_t seq_len, int32_t h_t, int32_t kv_t, int32_t head_dim, int64_t ldq,
+                     int64_t ldkv, int64_t ldo, int32_t causal, void* hip_stream) {
+  const char* fn = "tp_attn_core_fwd";
+  if (n_seq < 0 || seq_len < 0 || n_seq > 65535 || seq_len > 0x7FFFFFFF)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_seq / seq_len out of range", fn);
+  if (h_t <= 0 || kv_t <= 0 || h_t % kv_t || h_t > 65535)
+    return fail(TP_ERR_INVALID_ARG, "%s: h_t=%d must be a positive multiple of kv_t=%d", fn, h_t, kv_t);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TP_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", fn, head_dim);
+  if (causal != 0 && causal != 1) return fail(TP_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  if (ldq < (int64_t)h_t * head_dim || ldo < (int64_t)h_t * head_dim || ldkv < (int64_t)kv_t * head_dim)
+    return fail(TP_ERR_INVALID_ARG, "%s: leading dimension smaller than the heads it holds", fn);
+  if (ldq % 8 || ldkv % 8 || ldo % 8 || ldq > kMaxExtent || ldkv > kMaxExtent || ldo > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "%s: leading dimensions must be multiples of 8 and at most %lld", fn,
+                (long long)kMaxExtent);
+  if ((int64_t)seq_len * (ldq > ldkv ? ldq : ldkv) * 2 >= (int64_t(1) << 30))
+    return fail(TP_ERR_UNSUPPORTED, "%s: seq_len too long for one call", fn);
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(o, "o"));
+  if (n_seq * seq_len == 0) return TP_OK;
+  tpk::AttnDesc a{};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.o = (__bf16*)o;
+  a.n_seq = n_seq;
+  a.seq_len = (int32_t)seq_len;
+  a.head_dim = head_dim;
+  a.h_t = h_t;
+  a.kv_t = kv_t;
+  a.ldq = (int32_t)ldq;
+  a.ldkv = (int32_t)ldkv;
+  a.ldo = (int32_t)ldo;
+  a.causal = causal != 0;
+  return hip_status(tpk::launch_attention(a, (hipStream_t)hip_stream), "attention launch");
+}
+
 int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, const void* residual,
                    void* y, int64_t n_elems, int32_t part_dtype, int32_t out_dtype, void* hip_stream) {
   if (T_p < 1) return fail(TP_ERR_INVALID_ARG, "tp_partial_sum: T_p=%d < 1", T_p);

@@ -48,6 +48,8 @@ _SIGS = {
     "tp_attn_heads_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "tp_attn_heads_shard_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _vp]),
+    "tp_attn_core_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
+                                _i32, _vp]),
     "tp_partial_sum": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
 }
 
@@ -165,8 +167,15 @@ def tp_attn_heads_shard_fwd(x, wq, wk, wv, o_t, workspace, workspace_bytes, n_se
                             n_heads, n_kv_heads, head_dim, T_p, t, causal, hip_stream=None):
     _check("tp_attn_heads_shard_fwd", lib().tp_attn_heads_shard_fwd(
         _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(o_t), _ptr(workspace), workspace_bytes,
-        n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t, int(bool(causal)),
+        n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t, int(causal),
         _stream(hip_stream)))
+
+
+def tp_attn_core_fwd(q, k, v, o, n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv, ldo, causal,
+                     hip_stream=None):
+    _check("tp_attn_core_fwd", lib().tp_attn_core_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv, ldo,
+        int(causal), _stream(hip_stream)))
 
 
 def tp_partial_sum(partials, partial_stride, T_p, residual, y, n_elems, part_dtype, out_dtype,

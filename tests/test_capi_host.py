@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 1
@@ -121,4 +121,22 @@ def test_partial_sum_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_partial_sum(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_t=6, kv_t=4), S.TP_ERR_INVALID_ARG),
+    (dict(head_dim=96), S.TP_ERR_UNSUPPORTED),
+    (dict(ldq=100), S.TP_ERR_INVALID_ARG),
+    (dict(ldkv=772), S.TP_ERR_UNSUPPORTED),
+    (dict(causal=2), S.TP_ERR_INVALID_ARG),
+    (dict(q=None), S.TP_ERR_INVALID_ARG),
+    (dict(n_seq=-1), S.TP_ERR_INVALID_ARG),
+])
+def test_attn_core_rejects_before_launch(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, n_seq=1, seq_len=2048, h_t=6, kv_t=6, head_dim=128, ldq=768,
+             ldkv=768, ldo=768, causal=True, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_core_fwd(**a)
     assert e.value.code == code, S.tp_last_error()

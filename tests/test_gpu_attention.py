@@ -187,3 +187,30 @@ def test_attention_gqa_divisibility_rejected():
         S.tp_attn_heads_shard_fwd(x, w, w, w, o, o, o.numel() * 2, 1, 64, 128, 64, 8, 128, 16, 0,
                                   True)
     assert e.value.code == S.TP_ERR_NOT_DIVISIBLE
+
+
+@pytest.mark.parametrize("L,h_t,kv_t,dh,causal", [(300, 4, 2, 128, True), (96, 2, 2, 64, False),
+                                                  (2048, 6, 6, 128, True)])
+def test_attention_core_parity_strided(L, h_t, kv_t, dh, causal):
+    """tp_attn_core_fwd on projected heads stored with padded leading dimensions."""
+    n_seq = 2 if L < 2048 else 1
+    T = n_seq * L
+    ldq, ldkv, ldo = h_t * dh + 16, kv_t * dh + 8, h_t * dh + 24
+    g = np.random.default_rng(L + h_t)
+    q = I.bf16_bits(g.standard_normal((T, ldq)).astype(np.float32))
+    k = I.bf16_bits(g.standard_normal((T, ldkv)).astype(np.float32))
+    v = I.bf16_bits(g.standard_normal((T, ldkv)).astype(np.float32))
+    o = torch.full((T, ldo), 5.0, dtype=torch.bfloat16, device="cuda:0")
+    S.tp_attn_core_fwd(dev(q, I.BF16), dev(k, I.BF16), dev(v, I.BF16), o, n_seq, L, h_t, kv_t, dh,
+                       ldq, ldkv, ldo, causal)
+    torch.cuda.synchronize()
+    og = host64(o)
+    q64, k64, v64 = (f64(a, I.BF16) for a in (q, k, v))
+    for s in range(n_seq):
+        r = slice(s * L, (s + 1) * L)
+        for j in range(h_t):
+            kv = j // (h_t // kv_t)
+            ref = O.attention_head(q64[r, j * dh:(j + 1) * dh], k64[r, kv * dh:(kv + 1) * dh],
+                                   v64[r, kv * dh:(kv + 1) * dh], causal=causal)
+            assert nerr(og[r, j * dh:(j + 1) * dh], ref) <= BF16_TOL, (s, j)
+    assert np.all(og[:, h_t * dh:] == 5.0)          # padding columns untouched
