@@ -312,25 +312,32 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
   __bf16* q = (__bf16*)workspace;
   __bf16* k = q + T * h_t * head_dim;
   __bf16* v = k + T * kv_t * head_dim;
-  // Q, K, V column blocks of the rank's heads (column-parallel projections, no activation)
-  struct Proj { const void* w; __bf16* out; int64_t heads_total, heads_rank; } proj[3] = {
-      {wq, q, n_heads, h_t}, {wk, k, n_kv_heads, kv_t}, {wv, v, n_kv_heads, kv_t}};
-  for (const Proj& p : proj) {
-    tpk::GemmDesc g{};
-    g.A = x;
-    g.B0 = (const __bf16*)p.w + (size_t)t * p.heads_rank * head_dim;
-    g.B1 = nullptr;
-    g.C = p.out;
-    g.M = T;
-    g.N = (int32_t)(p.heads_rank * head_dim);
-    g.K = (int32_t)d;
-    g.lda = (int32_t)d;
-    g.ldb = (int32_t)(p.heads_total * head_dim);
-    g.ldc = g.N;
-    g.act = TP_ACT_NONE;
-    g.out_f32 = false;
-    TRY(hip_status(tpk::launch_gemm_bf16(g, s), "QKV projection GEMM launch"));
+  // Q, K, V column blocks of the rank's heads (column-parallel projections, no activation),
+  // as one launch over three column segments that share X.
+  tpk::GemmDesc g{};
+  g.A = x;
+  g.B0 = (const __bf16*)wq + (size_t)t * h_t * head_dim;
+  g.B1 = nullptr;
+  g.C = q;
+  g.M = T;
+  g.N = (int32_t)(h_t * head_dim);
+  g.K = (int32_t)d;
+  g.lda = (int32_t)d;
+  g.ldb = (int32_t)(n_heads * head_dim);
+  g.ldc = g.N;
+  g.act = TP_ACT_NONE;
+  g.out_f32 = false;
+  g.nseg = 3;
+  const void* wkv[2] = {wk, wv};
+  __bf16* outs[2] = {k, v};
+  for (int i = 0; i < 2; ++i) {
+    g.Bx[i] = (const __bf16*)wkv[i] + (size_t)t * kv_t * head_dim;
+    g.Cx[i] = outs[i];
+    g.Nx[i] = (int32_t)(kv_t * head_dim);
+    g.ldbx[i] = (int32_t)(n_kv_heads * head_dim);
+    g.ldcx[i] = g.Nx[i];
   }
+  TRY(hip_status(tpk::launch_gemm_bf16(g, s), "QKV projection GEMM launch"));
   tpk::AttnDesc a{};
   a.q = q;
   a.k = k;

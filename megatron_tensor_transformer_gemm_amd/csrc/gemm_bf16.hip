@@ -181,13 +181,31 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  // column segment of this tile (all values wave-uniform)
+  const void* Bseg = g.B0;
+  void* Cseg = g.C;
+  int N_ = g.N, ldb_ = g.ldb, ldc_ = g.ldc;
+  if (!DUAL && g.nseg > 1) {
+    const int t0 = (g.N + BNS - 1) / BNS;
+    if (tn >= t0) {
+      tn -= t0;
+      const int t1 = (g.Nx[0] + BNS - 1) / BNS;
+      const int sg = (g.nseg > 2 && tn >= t1) ? 1 : 0;
+      if (sg) tn -= t1;
+      Bseg = g.Bx[sg];
+      Cseg = g.Cx[sg];
+      N_ = g.Nx[sg];
+      ldb_ = g.ldbx[sg];
+      ldc_ = g.ldcx[sg];
+    }
+  }
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BNS;
   const int64_t rows_left64 = g.M - m0;
   const int rows_left = rows_left64 < BM ? (int)rows_left64 : BM;
 
   const __bf16* A = (const __bf16*)g.A + m0 * g.lda;
-  const __bf16* B0 = (const __bf16*)g.B0 + n0;
+  const __bf16* B0 = (const __bf16*)Bseg + n0;
   const __bf16* B1 = DUAL ? (const __bf16*)g.B1 + n0 : B0;
 
   // ---- per-lane global->LDS descriptors (fixed over the k loop).  Lanes whose row (A)
@@ -211,7 +229,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
     const int pos = (q % QSUB) * 64 + lane;
     const int row = pos / CPR;
     const int c = (pos % CPR) ^ (swz_b(row) & (CPR - 1));
-    b_voff[i] = (n0 + 8 * c < g.N) ? (uint32_t)(row * g.ldb + 8 * c) * 2u : kOOB;
+    b_voff[i] = (n0 + 8 * c < N_) ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
     b_kr[i] = row;
   }
   // B sub-tile a wave's copies land in is the same for all of its copies.
@@ -221,7 +239,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
     const int k0 = kt * BK;
     const bool full = k0 + BK <= g.K;
     const i32x4 da = make_desc(A + k0);
-    const i32x4 db = make_desc((b_second ? B1 : B0) + (int64_t)k0 * g.ldb);
+    const i32x4 db = make_desc((b_second ? B1 : B0) + (int64_t)k0 * ldb_);
     const uint32_t lds = (uint32_t)(uintptr_t)base;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
@@ -353,7 +371,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn * WCOLS + nb * 32 + 8 * q + 4 * (lane >> 5);
-        if (n >= g.N) continue;
+        if (n >= N_) continue;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -362,10 +380,10 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
           v[e] = epilogue<ACT>(u, w);
         }
         if constexpr (OUT_F32) {
-          float* c = (float*)g.C + m * g.ldc + n;
+          float* c = (float*)Cseg + m * ldc_ + n;
           *(f32x4*)c = f32x4{v[0], v[1], v[2], v[3]};
         } else {
-          __bf16* c = (__bf16*)g.C + m * g.ldc + n;
+          __bf16* c = (__bf16*)Cseg + m * ldc_ + n;
           *(bf16x4*)c = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         }
       }
@@ -377,7 +395,8 @@ template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32>
 hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? BN / 2 : BN;
   const int64_t tm = (g.M + BM - 1) / BM;
-  const int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
+  int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
+  for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) tn += (g.Nx[i] + OUT_BN - 1) / OUT_BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, DUAL, ACT, OUT_F32>),
                      dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, g, (int)tm, (int)tn);
@@ -390,7 +409,9 @@ hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
 template <bool DUAL, int ACT, bool OUT_F32>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
-  const int64_t big = ((g.M + 255) / 256) * ((g.N + OUT_BN - 1) / OUT_BN);
+  int64_t ncols = g.N;
+  for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) ncols += g.Nx[i];
+  const int64_t big = ((g.M + 255) / 256) * ((ncols + OUT_BN - 1) / OUT_BN);
   if (big >= 256) {
     if (g.K > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32>(g, s);
     return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32>(g, s);

@@ -11,6 +11,9 @@ enum Act : int { kActNone = 0, kActGelu = 1, kActSwiglu = 2, kActBilinear = 3 };
 
 // C[M, N] = epilogue(A[M, K] . B0[K, N] (, A . B1[K, N])), all row-major.
 // B0/B1 point at the first element of the rank's block (offsets already applied).
+// Up to two more column segments (nseg > 1, ungated activations only) extend the output
+// columns: segment i multiplies the same A by Bx[i] [K, Nx[i]] into Cx[i] -- one launch
+// for several products that share A (the Q, K and V projections).
 struct GemmDesc {
   const void* A;
   const void* B0;
@@ -21,6 +24,10 @@ struct GemmDesc {
   int32_t lda, ldb, ldc;
   int act;
   bool out_f32;
+  int32_t nseg = 1;
+  const void* Bx[2] = {nullptr, nullptr};
+  void* Cx[2] = {nullptr, nullptr};
+  int32_t Nx[2] = {0, 0}, ldbx[2] = {0, 0}, ldcx[2] = {0, 0};
 };
 
 // bf16 inputs, fp32 accumulation on MFMA; output bf16 (or fp32 if out_f32).
