@@ -5,18 +5,32 @@
 // O_j = softmax(Q_j K_j^T / sqrt(d_h) [+ causal mask]) V_j for each local query head j,
 // grouped-query heads reading KV head j / (h_t / kv_t), each sequence on its own.
 //
-// One workgroup = 2 waves = 64 queries of one head of one sequence; each wave owns 32
-// queries.  Keys are visited in blocks of 64 with a running (online) softmax:
+// One workgroup = 8 waves = 64 queries of one head of one sequence.  A rank holds few
+// heads, so there are few such query blocks; to keep the CUs busy the keys are split as
+// well: the waves form 4 key groups of 2, group g visits the 32-key blocks g, g+4, g+8, ...
+// and inside a group each wave owns 32 of the 64 queries.  Both waves of a group read the
+// same K/V block from LDS, so every byte brought from L2 feeds 64 queries.
 //   S^T = K . Q^T         v_mfma_f32_32x32x16_bf16, keys on the rows, queries on the
 //                          columns, so each lane holds one query's scores;
-//   P^T = exp2(S^T - m)   row statistics need one exchange between lanes l and l^32;
+//   P^T = exp2(S^T - m)   running (online) softmax in base 2 with the 1/sqrt(d_h) scale
+//                          folded into one FMA; row statistics combine lanes l and l^32
+//                          with v_permlane32_swap;
 //   O^T += V^T . P^T      P^T is already in the B-operand layout (the key order inside
 //                          each 16-key step is the same permutation on both operands);
 //                          V stays row-major in LDS and ds_read_b64_tr_b16 delivers
 //                          V^T fragments.
-// K and V blocks stream HBM/L2 -> LDS with buffer_load ... lds into two stages.  Keys
-// beyond the sequence come back as zeros and are masked to -inf.
+// The softmax is VALU work (a quarter-rate exp per score) of about the same length as the
+// two products, so each wave runs it one block behind: while the MFMAs of block i's S^T
+// run, the VALU turns block i-1's scores into P^T, then block i-1's O^T update follows.
+// V therefore lags K by one block in the LDS stages.  The running maximum moves only when
+// a block exceeds it by more than 2^8 (the exponentials stay below 256, the sums exact),
+// so the O^T rescale is rare after the first blocks.
+// K and V blocks stream L2 -> LDS with buffer_load ... lds, two stages each; keys beyond
+// the sequence come back as zeros and are masked to -inf.  At the end the four groups'
+// partial states (m, l, O^T) meet in LDS: wave (g, half) rescales and sums the four
+// partials of head-dimension block g of its 32 queries and stores it.
 #include "tp_internal.h"
+#include "lds_copy.h"
 
 namespace tpk {
 namespace {
@@ -25,243 +39,360 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_raw __attribute__((__vector_size__(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBQ = 64;     // queries per workgroup (2 waves x 32)
-constexpr int kBKV = 64;    // keys per block
-constexpr uint32_t kOOB = 0x40000000u;
-constexpr int kNumRecords = 0x40000000;
-constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kWaves = 8;
+constexpr int kGroups = 4;     // key groups of 2 waves
+constexpr int kBQ = 64;        // queries per workgroup
+constexpr int kBK = 32;        // keys per block
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords,
-                                           kRsrcWord3);
-}
-
-// K tile [64 keys][DH]: chunk c of row r stored at c ^ (r & 15) (mod chunks per row).
+// K block [32 keys][DH]: chunk c of row r stored at c ^ (r mod chunks-per-row, mod 16).
 template <int CPR>
 __device__ __forceinline__ int swz_k(int r) { return r & (CPR - 1) & 15; }
-// V tile [64 keys][DH], read by 4-row transposing reads: XOR pattern by row mod 4.
+// V block [32 keys][DH], read by 4-row transposing reads: XOR pattern by row mod 4.
 __device__ __forceinline__ int swz_v(int r) { return (0xCA60 >> (4 * (r & 3))) & 15; }
 
-__device__ __forceinline__ float xor32(float v) {
-  return __shfl_xor(v, 32, 64);
+// Combine the values of lanes l and l^32 (the two halves of a score column).
+__device__ __forceinline__ float max_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DH>
-__global__ void __launch_bounds__(128) attention_kernel(AttnDesc a) {
-  constexpr int CPR = DH / 8;                 // 16-byte chunks per row
-  constexpr int ROWB = DH * 2;                // bytes per row
-  constexpr int TILE = kBKV * ROWB;           // bytes of one K or V tile
-  constexpr int LD_PER_WAVE = TILE / 1024 / 2;
-  constexpr int KS = DH / 16;                 // 16-wide k-steps over the head dimension
-  constexpr int DB = DH / 32;                 // 32-row blocks of O^T
-  static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
-  __shared__ __attribute__((aligned(1024))) unsigned char kv0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char kv1[2 * TILE];
+constexpr float kLazy = 8.0f;  // log2 of the largest exponential kept before rescaling
+
+template <int DH>
+__global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int nqb) {
+  constexpr int CPR = DH / 8;           // 16-byte chunks per row
+  constexpr int ROWB = DH * 2;          // bytes per row
+  constexpr int TILE = kBK * ROWB;      // one K or V block
+  constexpr int NC = TILE / 1024 / 2;   // 1 KiB copies per wave per block
+  constexpr int KS = DH / 16;           // 16-wide k-steps over the head dimension
+  constexpr int DB = DH / 32;           // 32-row blocks of O^T
+  constexpr int SLOT = 32 * 32 * 4;     // one fp32 32x32 block of O^T
+  static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
+  static_assert(2 * TILE == DB * SLOT, "two stages hold one half's partials");
+
+  // K and V stages: [stage][group][block].  After the key loop kst holds the partial
+  // O^T blocks of the first 32 queries, vst those of the second.
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[2 * kGroups * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst[2 * kGroups * TILE];
+  __shared__ f32x2 ml[2 * kGroups * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wave >> 1;    // key group
+  const int qh = wave & 1;    // which 32 of the 64 queries
   const int S = a.seq_len;
-  const int nqb = (S + kBQ - 1) / kBQ;
-  const int qb = nqb - 1 - (int)blockIdx.x;   // heaviest (latest) query blocks first
-  const int j = blockIdx.y;                   // local query head
-  const int64_t seq = blockIdx.z;
+  const int qb = nqb - 1 - (int)(blockIdx.x / (unsigned)a.h_t);  // latest (heaviest) first
+  const int j = (int)(blockIdx.x % (unsigned)a.h_t);              // local query head
+  const int64_t seq = blockIdx.y;
   const int kvh = j / (a.h_t / a.kv_t);
   const int q0 = qb * kBQ;
-  const int64_t row0 = seq * (int64_t)S;      // first token row of this sequence
+  const int64_t row0 = seq * (int64_t)S;   // first token row of this sequence
 
   const __bf16* Qp = a.q + row0 * a.ldq + (int64_t)j * DH;
   const __bf16* Kp = a.k + row0 * a.ldkv + (int64_t)kvh * DH;
   const __bf16* Vp = a.v + row0 * a.ldkv + (int64_t)kvh * DH;
 
   // ---- Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
-  const int qrow = q0 + wave * 32 + (lane & 31);
+  const int qrow = q0 + 32 * qh + (lane & 31);
   bf16x8 qf[KS];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qp);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(Qp), (short)0, kNumRecords, kRsrcWord3);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t off =
           qrow < S ? (uint32_t)((int64_t)qrow * a.ldq + 16 * ks + 8 * (lane >> 5)) * 2u : kOOB;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
+    // Retire these loads here: a wait for them inside the key loop would also wait for the
+    // copies of the next block, which are in flight there.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  // ---- K/V copy descriptors: copy q of a tile covers rows 1024/ROWB * q ..
-  uint32_t ld_off[LD_PER_WAVE];
-  int ld_row[LD_PER_WAVE];
+  LDS_AS unsigned char* KST = (LDS_AS unsigned char*)kst;
+  LDS_AS unsigned char* VST = (LDS_AS unsigned char*)vst;
+
+  // ---- copies: the two waves of a group each bring half of the group's K and V blocks.
+  // Copy i of this wave covers rows c_row0 + i*RPC.  The V swizzle depends on the row mod
+  // 4 only, so its offsets step by a constant; the K swizzle needs one offset per copy.
+  constexpr int RPC = 64 / CPR;          // rows per 1 KiB copy
+  const int c_row0 = (qh * NC * 64 + lane) / CPR, c_slot = lane % CPR;
+  uint32_t k_off[NC];
 #pragma unroll
-  for (int i = 0; i < LD_PER_WAVE; ++i) {
-    const int q = wave * LD_PER_WAVE + i;
-    const int pos = q * 64 + lane;
-    const int row = pos / CPR;
-    const int c = (pos % CPR) ^ swz_k<CPR>(row);
-    ld_off[i] = (uint32_t)(row * a.ldkv + 8 * c) * 2u;
-    ld_row[i] = row;
+  for (int i = 0; i < NC; ++i) {
+    const int row = c_row0 + i * RPC;
+    k_off[i] = (uint32_t)(row * a.ldkv + 8 * (c_slot ^ swz_k<CPR>(row))) * 2u;
   }
-  // V copies use the V swizzle.
-  uint32_t lv_off[LD_PER_WAVE];
+  const uint32_t v_off0 = (uint32_t)(c_row0 * a.ldkv + 8 * (c_slot ^ (swz_v(c_row0) & (CPR - 1)))) * 2u;
+  const uint32_t copy_step = (uint32_t)(RPC * a.ldkv) * 2u;
+  static_assert(RPC % 4 == 0, "V swizzle period");
+  const int kend = a.causal ? (q0 + kBQ < S ? q0 + kBQ : S) : S;
+  const int nkb = (kend + kBK - 1) / kBK;
+  const int nit = (nkb + kGroups - 1) / kGroups;   // same for every wave
+
+  // Block g + 4*it of this group (its K or its V) into stage it % 2.  Past the last block
+  // every lane is masked (zeros), so the product code runs unconditionally on
+  // well-defined data.
+  auto issue = [&](int it, bool is_v) {
+    const int key0 = (g + kGroups * it) * kBK;
+    const int lim = key0 < kend ? S - key0 : 0;
+    const i32x4 desc = make_desc((is_v ? Vp : Kp) + (int64_t)key0 * a.ldkv);
+    const uint32_t base =
+        (uint32_t)(uintptr_t)((is_v ? VST : KST) + ((it & 1) * kGroups + g) * TILE);
 #pragma unroll
-  for (int i = 0; i < LD_PER_WAVE; ++i) {
-    const int q = wave * LD_PER_WAVE + i;
-    const int pos = q * 64 + lane;
-    const int row = pos / CPR;
-    const int c = (pos % CPR) ^ (swz_v(row) & (CPR - 1));
-    lv_off[i] = (uint32_t)(row * a.ldkv + 8 * c) * 2u;
-  }
-  auto issue = [&](int kb, LDS_AS unsigned char* base) {
-    const int key0 = kb * kBKV;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp + (int64_t)key0 * a.ldkv);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp + (int64_t)key0 * a.ldkv);
-#pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) {
-      const uint32_t v = key0 + ld_row[i] < S ? ld_off[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (LDS_AS void*)(base + (wave * LD_PER_WAVE + i) * 1024), 16, v, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) {
-      const uint32_t v = key0 + ld_row[i] < S ? lv_off[i] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (LDS_AS void*)(base + TILE + (wave * LD_PER_WAVE + i) * 1024), 16, v, 0, 0, 0);
+    for (int i = 0; i < NC; ++i) {
+      const uint32_t off = is_v ? v_off0 + i * copy_step : k_off[i];
+      copy16_to_lds(desc, c_row0 < lim - i * RPC ? off : kOOB,
+                    __builtin_amdgcn_readfirstlane(base + (qh * NC + i) * 1024));
     }
   };
+  auto stage = [&](LDS_AS unsigned char* stages, int it) -> const LDS_AS unsigned char* {
+    return stages + ((it & 1) * kGroups + g) * TILE;
+  };
 
-  // ---- per-lane LDS read offsets
-  // K (A operand of S^T): row = kblk*32 + lane%32, chunk 2*ks + lane/32
+  // ---- per-lane LDS read offsets.  The XOR swizzles touch address bits inside a row
+  // only, so the offset of k-step ks (of head-dim block d) is the base XOR a constant.
+  // K (A operand of S^T): row = lane % 32, chunk 2*ks + lane / 32
   const int krow = lane & 31;
-  // V^T (A operand of O^T): 16-lane group g reads 4 key rows x 16 dh columns
+  const uint32_t k_rd = (uint32_t)(krow * ROWB + (((lane >> 5) ^ swz_k<CPR>(krow)) << 4));
+  // V^T (A operand of O^T): 16-lane group g4 reads 4 key rows x 16 head-dim columns; the
+  // second read of a fragment is 8 rows further.
   const int g4 = lane >> 4, i16 = lane & 15;
-  const int vrow_l = 4 * (g4 >> 1) + (i16 >> 2);      // + 32*kblk + 16*h (+8 for the 2nd read)
+  const int vrow_l = 4 * (g4 >> 1) + (i16 >> 2);
   const int vsw = swz_v(vrow_l) & (CPR - 1);
+  const int vn = 16 * (g4 & 1) + 4 * (i16 & 3);
+  const uint32_t v_rd = (uint32_t)(vrow_l * ROWB + (((vn >> 3) ^ vsw) << 4) + ((vn >> 2) & 1) * 8);
+  static_assert(ROWB >= 128 && (ROWB & (ROWB - 1)) == 0, "row pitch");
 
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;   // running max (scaled, log2 units) and sum
   const float scale = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
+  const int qmin = q0 + 32 * qh;                                 // this wave's first query
 
-  const int kend = a.causal ? (q0 + kBQ < S ? q0 + kBQ : S) : S;
-  const int nkb = (kend + kBKV - 1) / kBKV;
-
-  auto block = [&](int kb, const LDS_AS unsigned char* Ks) {
-    const LDS_AS unsigned char* Vs = Ks + TILE;
-    const int key0 = kb * kBKV;
-    // S^T for 2 blocks of 32 keys
-    f32x16 s[2];
+  // Does block `it` of this group reach past the sequence or the diagonal?
+  auto needs_mask = [&](int it) {
+    const int key0 = (g + kGroups * it) * kBK;
+    return key0 + kBK > S || (a.causal && key0 + kBK - 1 > qmin);
+  };
+  auto read_k = [&](const LDS_AS unsigned char* Ks, bf16x8 (&kf)[KS]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      s[h] = f32x16{};
-      const int r = h * 32 + krow;
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const LDS_AS bf16x8*)(Ks + (k_rd ^ (ks << 5)));
+  };
+  auto read_v = [&](const LDS_AS unsigned char* Vs, bf16x8 (&vf)[2][DB]) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = 2 * ks + (lane >> 5);
-        const bf16x8 kf =
-            *(const LDS_AS bf16x8*)(Ks + r * ROWB + ((c ^ swz_k<CPR>(r)) << 4));
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[h], 0, 0, 0);
-      }
-    }
-    // mask, scale, running max (this lane's query: qrow)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * h + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const bool masked = key >= S || (a.causal && key > qrow);
-        const float v = masked ? -INFINITY : s[h][r] * scale;
-        s[h][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float sum = 0.0f;
-    bf16x8 pf[4];   // P^T fragments: 16-key steps (h, half)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(s[h][8 * hf + e] - m_use);
-          sum += p;
-          pf[2 * h + hf][e] = (__bf16)p;
-        }
-    sum += xor32(sum);
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < DB; ++d) o[d] *= alpha;
-    // O^T += V^T . P^T over 4 steps of 16 keys
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int h = st >> 1, hf = st & 1;
-      const int rbase = 32 * h + 16 * hf + vrow_l;
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        const int n = d * 32 + 16 * (g4 & 1) + 4 * (i16 & 3);
-        const int coff = (((n >> 3) ^ vsw) << 4) + ((n >> 2) & 1) * 8;
-        const LDS_AS unsigned char* p0 = Vs + rbase * ROWB + coff;
+        const LDS_AS unsigned char* p0 = Vs + 16 * hf * ROWB + (v_rd ^ (d << 6));
         bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)p0);
         bf16x4_raw hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p0 + 8 * ROWB));
-        const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[d], 0, 0, 0);
+        vf[hf][d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+  };
+  auto qk = [&](const bf16x8 (&kf)[KS]) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    return s;
+  };
+  auto pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pf)[2]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[hf][d], pf[hf], o[d], 0, 0, 0);
+  };
+  // Scores of block `it` (raw S^T) -> P^T fragments; updates m_run and l_run.  Returns
+  // whether O^T must be rescaled by `alpha` (the same answer on every lane).
+  auto softmax = [&](auto mask_t, f32x16 s, int it, bf16x8 (&pf)[2], float& alpha) {
+    if constexpr (decltype(mask_t)::value) {
+      const int key0 = (g + kGroups * it) * kBK;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (key >= S || (a.causal && key > qrow)) s[r] = -INFINITY;
       }
     }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = max_pair(mx) * scale;
+    const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0;
+    const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float sum = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hf + e], scale, -m_use));
+        sum += p;
+        pf[hf][e] = (__bf16)p;
+      }
+    l_run = __builtin_fmaf(l_run, alpha, sum_pair(sum));
+    return grow;
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d] *= alpha;
   };
 
-  LDS_AS unsigned char* S0 = (LDS_AS unsigned char*)kv0;
-  LDS_AS unsigned char* S1 = (LDS_AS unsigned char*)kv1;
-  issue(0, S0);
-  int kb = 0;
-  for (; kb + 1 < nkb; kb += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue(kb + 1, S1);
-    block(kb, S0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 2 < nkb) issue(kb + 2, S0);
-    block(kb + 1, S1);
+  // ---- key loop: iteration it multiplies S^T of block it and finishes block it-1
+  issue(0, false);
+  sync_copies<0>();
+  if (nit > 1) issue(1, false);
+  issue(0, true);
+  f32x16 s_a, s_b;
+  {
+    bf16x8 kf[KS];
+    read_k(stage(KST, 0), kf);
+    s_a = qk(kf);
   }
-  if (kb < nkb) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    block(kb, S0);
+  // One iteration: scores s_in of block it-1 -> P^T and the O^T update, while the MFMAs
+  // produce s_out, the scores of block it.
+  auto step = [&](auto mask_t, int it, const f32x16& s_in, f32x16& s_out) {
+    // K of block it and V of block it-1 have landed; every wave is done with the
+    // previous iteration's stages
+    sync_copies<0>();
+    if (it + 1 < nit) issue(it + 1, false);
+    issue(it, true);
+    bf16x8 pf[2];
+    float alpha;
+    bool grow;
+    {
+      bf16x8 kf[KS];
+      read_k(stage(KST, it), kf);
+      s_out = qk(kf);
+      grow = softmax(mask_t, s_in, it - 1, pf, alpha);
+    }
+    // V fragments only now: they take the K fragments' registers
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 vf[2][DB];
+    read_v(stage(VST, it - 1), vf);
+    if (grow) rescale(alpha);
+    pv(vf, pf);
+  };
+  // Blocks that need a mask (past the diagonal or the sequence end) come last; the loop
+  // over the others is unrolled by two so the score registers alternate without copies.
+  int it = 1;
+  int it_nm = 1;   // first iteration whose finished block needs a mask
+  while (it_nm < nit && !needs_mask(it_nm - 1)) ++it_nm;
+  for (; it + 1 < it_nm; it += 2) {
+    step(Flag<false>{}, it, s_a, s_b);
+    step(Flag<false>{}, it + 1, s_b, s_a);
+  }
+  if (it < it_nm) {
+    step(Flag<false>{}, it, s_a, s_b);
+    s_a = s_b;
+    ++it;
+  }
+  for (; it < nit; ++it) {
+    step(Flag<true>{}, it, s_a, s_b);
+    s_a = s_b;
+  }
+  sync_copies<0>();
+  {
+    bf16x8 vf[2][DB], pf[2];
+    read_v(stage(VST, nit - 1), vf);
+    float alpha;
+    const bool grow = needs_mask(nit - 1) ? softmax(Flag<true>{}, s_a, nit - 1, pf, alpha)
+                                          : softmax(Flag<false>{}, s_a, nit - 1, pf, alpha);
+    if (grow) rescale(alpha);
+    pv(vf, pf);
   }
 
-  // ---- O = O^T / l, one 8-byte store per 4 consecutive head dims
-  if (qrow < S) {
-    const float inv = 1.0f / l_run;
-    __bf16* Op = a.o + (row0 + qrow) * a.ldo + (int64_t)j * DH;
+  // ---- combine the four groups' partial states
+  sync_copies<0>();
+  LDS_AS unsigned char* half = qh ? VST : KST;
+  ((LDS_AS f32x2*)ml)[(qh * kGroups + g) * 64 + lane] = f32x2{m_run, l_run};
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+  for (int d = 0; d < DB; ++d)
+    if (d != g) {
+      LDS_AS f32x4* p = (LDS_AS f32x4*)(half + (g * DB + d) * SLOT);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dh = d * 32 + 8 * g + 4 * (lane >> 5);
-        *(bf16x4*)(Op + dh) = bf16x4{(__bf16)(o[d][4 * g] * inv), (__bf16)(o[d][4 * g + 1] * inv),
-                                     (__bf16)(o[d][4 * g + 2] * inv), (__bf16)(o[d][4 * g + 3] * inv)};
-      }
+      for (int r4 = 0; r4 < 4; ++r4)
+        p[r4 * 64 + lane] = f32x4{o[d][4 * r4], o[d][4 * r4 + 1], o[d][4 * r4 + 2], o[d][4 * r4 + 3]};
+    }
+  sync_copies<0>();
+  if (g >= DB) return;   // head_dim 64: groups 2 and 3 only contribute
+
+  float mg[kGroups], lg[kGroups];
+#pragma unroll
+  for (int h = 0; h < kGroups; ++h) {
+    const f32x2 t = ((const LDS_AS f32x2*)ml)[(qh * kGroups + h) * 64 + lane];
+    mg[h] = t[0];
+    lg[h] = t[1];
   }
+  float M = mg[0];
+#pragma unroll
+  for (int h = 1; h < kGroups; ++h) M = fmaxf(M, mg[h]);
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  float al[kGroups], L = 0.0f;
+#pragma unroll
+  for (int h = 0; h < kGroups; ++h) {
+    al[h] = __builtin_amdgcn_exp2f(mg[h] - Mu);
+    L += al[h] * lg[h];
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+    if (d == g) {
+      const float own = __builtin_amdgcn_exp2f(m_run - Mu);
+      f32x16 acc = o[d] * own;
+#pragma unroll
+      for (int h = 0; h < kGroups; ++h)
+        if (h != g) {
+          const LDS_AS f32x4* p = (const LDS_AS f32x4*)(half + (h * DB + d) * SLOT);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 t = p[r4 * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * r4 + i] += al[h] * t[i];
+          }
+        }
+      // O = O^T / l, one 8-byte store per 4 consecutive head dims
+      if (qrow < S) {
+        __bf16* Op = a.o + (row0 + qrow) * a.ldo + (int64_t)j * DH + 32 * d;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(bf16x4*)(Op + 8 * r4 + 4 * (lane >> 5)) =
+              bf16x4{(__bf16)(acc[4 * r4] * inv), (__bf16)(acc[4 * r4 + 1] * inv),
+                     (__bf16)(acc[4 * r4 + 2] * inv), (__bf16)(acc[4 * r4 + 3] * inv)};
+      }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnDesc& a, hipStream_t s) {
   if (a.seq_len <= 0 || a.n_seq <= 0) return hipSuccess;
-  if (a.n_seq > 65535 || a.h_t > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((a.seq_len + kBQ - 1) / kBQ), (unsigned)a.h_t, (unsigned)a.n_seq);
+  const int64_t nqb = (a.seq_len + kBQ - 1) / kBQ;
+  if (a.n_seq > 65535 || a.h_t <= 0 || nqb * a.h_t > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nqb * a.h_t), (unsigned)a.n_seq);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb);
   else if (a.head_dim == 64)
-    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -30,6 +30,7 @@
 //    is given a contiguous range of tiles in a grouped raster (4 tile rows),
 //    so concurrently running tiles of one XCD share A and B panels in its L2.
 #include "tp_internal.h"
+#include "lds_copy.h"
 
 namespace tpk {
 namespace {
@@ -43,40 +44,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;    // 4 waves
-constexpr uint32_t kOOB = 0x40000000u;       // voffset of a masked lane: >= num_records
-constexpr int kNumRecords = 0x40000000;      // every valid per-lane offset is below 1 GiB
-constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords,
-                                           kRsrcWord3);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor as four SGPRs, for the copy below.
-__device__ __forceinline__ i32x4 make_desc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xFFFF, kNumRecords, kRsrcWord3};
-}
-
-// One buffer_load_dwordx4 ... lds: each lane copies 16 bytes from desc+voff into
-// LDS at lds_base + 16*lane.  Issued as inline assembly so that the compiler does not
-// track the asynchronous LDS write: completion is managed explicitly (vmcnt + barrier),
-// which lets several stages stay in flight.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved, yet this asm does set it
-__device__ __forceinline__ void copy16_to_lds(const i32x4& desc, uint32_t voff,
-                                              uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(desc), "s"(lds_base)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Physical chunk of logical chunk c in B k-row r is c ^ swz_b(r): the four k-rows a
 // transposing read touches at once get disjoint chunk sets both in 32-byte pairs and in
@@ -118,14 +85,6 @@ template <int ACPR>
 __device__ __forceinline__ int swz_a(int r) {
   if constexpr (ACPR == 8) return (r ^ ((r >> 3) & 3)) & 7;
   else return ((r >> 2) ^ (r >> 1)) & 3;
-}
-
-// Workgroup barrier after this wave's copies have landed except for the newest I, and
-// its LDS reads have completed.  (A __syncthreads() would also wait for every copy in
-// flight: the fence it carries treats them as pending stores.)
-template <int I>
-__device__ __forceinline__ void sync_copies() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(I) : "memory");
 }
 
 // BK k per LDS stage, NST stages in flight.  The stage boundary is moved one 16-k substep
