@@ -131,6 +131,76 @@ def ffn_unsharded(x, w1, w3, w2, act: str) -> np.ndarray:
     return row_parallel(h, w2, (0, w2.shape[0]))
 
 
+# ----------------------------------------------------------------------------- FFN backward
+def gelu_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of u * Phi(u): Phi(u) + u * phi(u), phi the standard normal density."""
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * _sp.erfc(-u / math.sqrt(2.0)) + u * np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
+
+
+def silu_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of u * s(u), s the logistic function: s(u) * (1 + u * (1 - s(u)))."""
+    u = np.asarray(u, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * (1.0 - s))
+
+
+def act_backward(dh, u, v, act: str):
+    """(dU, dV) from dH and the saved pre-activations U = X W1(t), V = X W3(t).
+
+    The chain rule through the element-wise activation of the column shard:
+    gelu: dU = dH * gelu'(U); swiglu (H = silu(U) * V): dU = dH * V * silu'(U),
+    dV = dH * silu(U); bilinear (H = U * V): dU = dH * V, dV = dH * U; none: dU = dH.
+    dV is None for the ungated kinds.
+    """
+    dh = np.asarray(dh, dtype=np.float64)
+    if act == "none":
+        return dh, None
+    if act == "gelu":
+        return dh * gelu_grad(u), None
+    if act == "swiglu":
+        return dh * v * silu_grad(u), dh * silu(u)
+    if act == "bilinear":
+        return dh * v, dh * u
+    raise ValueError(act)
+
+
+def ffn_shard_bwd(x, w1, w3, w2, dy, T_p: int, t: int, act: str) -> dict:
+    """Rank t's share of the FFN backward, given dY = dL/dy for the full output y.
+
+    "7.9 Tensor and pipeline parallelism" section 2.1 (the f-g pattern): g, the
+    all-reduce after the row shard, is the identity going backward, so every
+    rank receives the whole dY; f, the identity before the column shard, becomes
+    an all-reduce, so rank t's input gradient dX(t) is a partial sum and
+    dX = sum_t dX(t).  The weight gradients of a rank touch only its own blocks.
+    With U = X W1(t), V = X W3(t), H = sigma(U[, V]) and y(t) = H W2(t):
+        dH = dY W2(t)^T          dW2(t) = H^T dY          (rows cols(t) of dW2)
+        (dU, dV) = act_backward(dH, U, V)
+        dX(t) = dU W1(t)^T [+ dV W3(t)^T]
+        dW1(t) = X^T dU [, dW3(t) = X^T dV]             (columns cols(t))
+    Returns every intermediate: u, v, h, dh, du, dv, dx_t, dw1, dw3, dw2.
+    """
+    d_ff = w1.shape[1]
+    b, n = shard_range(d_ff, T_p, t)
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    w1c = np.asarray(w1[:, b:b + n], dtype=np.float64)
+    w2r = np.asarray(w2[b:b + n, :], dtype=np.float64)
+    gated = act in ("swiglu", "bilinear")
+    w3c = np.asarray(w3[:, b:b + n], dtype=np.float64) if gated else None
+    u = x @ w1c
+    v = x @ w3c if gated else None
+    h = column_parallel(x, w1, w3, (b, b + n), act)
+    dh = dy @ w2r.T
+    dw2 = h.T @ dy
+    du, dv = act_backward(dh, u, v, act)
+    dx_t = du @ w1c.T
+    if gated:
+        dx_t = dx_t + dv @ w3c.T
+    return {"u": u, "v": v, "h": h, "dh": dh, "du": du, "dv": dv, "dx_t": dx_t,
+            "dw1": x.T @ du, "dw3": x.T @ dv if gated else None, "dw2": dw2}
+
+
 def partial_sum(parts, residual=None) -> np.ndarray:
     """y = sum_t y(t) [+ residual] -- what the all-reduce g computes.
 

@@ -10,6 +10,7 @@ import math
 import numpy as np
 import pytest
 
+import test_oracle_backward as bpins
 import test_oracle_pins as pins
 from oracle import tp_oracle as O
 
@@ -72,6 +73,45 @@ def _transposed_w2(h, w2, rows):
     return np.asarray(h, dtype=np.float64) @ blk
 
 
+def _gelu_grad_cdf_only(u):
+    """Drops the u*phi(u) term of gelu'."""
+    from scipy import special
+    return 0.5 * special.erfc(-np.asarray(u, dtype=np.float64) / math.sqrt(2.0))
+
+
+def _silu_grad_sign(u):
+    u = np.asarray(u, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * s)
+
+
+_orig_act_backward = O.act_backward
+
+
+def _swiglu_bwd_without_gate(dh, u, v, act):
+    du, dv = _orig_act_backward(dh, u, v, act)
+    if act == "swiglu":
+        du = np.asarray(dh, dtype=np.float64) * O.silu_grad(u)
+    return du, dv
+
+
+_orig_ffn_shard_bwd = O.ffn_shard_bwd
+
+
+def _dx_without_w3_term(x, w1, w3, w2, dy, T_p, t, act):
+    g = dict(_orig_ffn_shard_bwd(x, w1, w3, w2, dy, T_p, t, act))
+    if g["dv"] is not None:
+        b, n = O.shard_range(w1.shape[1], T_p, t)
+        g["dx_t"] = g["du"] @ np.asarray(w1[:, b:b + n], dtype=np.float64).T
+    return g
+
+
+def _dw2_from_preactivation(x, w1, w3, w2, dy, T_p, t, act):
+    g = dict(_orig_ffn_shard_bwd(x, w1, w3, w2, dy, T_p, t, act))
+    g["dw2"] = g["u"].T @ np.asarray(dy, dtype=np.float64)
+    return g
+
+
 MUTATIONS = [
     ("silu", _wrong_silu_sign, [lambda: pins.test_silu_closed_forms_and_library(),
                                 lambda: pins.test_brute_force_tiny("swiglu", 2)]),
@@ -84,6 +124,14 @@ MUTATIONS = [
     ("attention_head", _mask_diagonal_too, [lambda: pins.test_attention_special_cases(),
                                             lambda: pins.test_attention_brute_force()]),
     ("row_parallel", _transposed_w2, [lambda: pins.test_brute_force_tiny("none", 2)]),
+    ("gelu_grad", _gelu_grad_cdf_only, [lambda: bpins.test_activation_derivative_matches_finite_differences(
+        "gelu", "gelu_grad"), lambda: bpins.test_backward_matches_torch_autograd_fp64("gelu", 1)]),
+    ("silu_grad", _silu_grad_sign, [lambda: bpins.test_activation_derivative_closed_forms(),
+                                    lambda: bpins.test_backward_matches_finite_differences("swiglu")]),
+    ("act_backward", _swiglu_bwd_without_gate, [lambda: bpins.test_backward_matches_finite_differences("swiglu"),
+                                                lambda: bpins.test_backward_matches_torch_autograd_fp64("swiglu", 4)]),
+    ("ffn_shard_bwd", _dx_without_w3_term, [lambda: bpins.test_backward_matches_finite_differences("bilinear")]),
+    ("ffn_shard_bwd", _dw2_from_preactivation, [lambda: bpins.test_backward_matches_torch_autograd_fp64("gelu", 4)]),
 ]
 
 
