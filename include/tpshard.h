@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TPSHARD_ABI_VERSION 1
+#define TPSHARD_ABI_VERSION 2
 
 /* Status codes. */
 #define TP_OK                 0
@@ -139,6 +139,61 @@ int tp_ffn_column_fwd(const void* x, const void* w1, const void* w3, void* h_t,
 int tp_ffn_row_fwd(const void* h_t, const void* w2, void* y_t,
                    int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
                    int32_t in_dtype, int32_t out_dtype, void* hip_stream);
+
+/*
+ * Training forward of rank t's FFN share: tp_ffn_shard_fwd in bf16 that also
+ * keeps what the backward needs, in caller-owned buffers.
+ *
+ *   h_t       [T, n] bf16, n = d_ff/T_p: H(t), the activation output (input of W2(t))
+ *   u_t       [T, n] bf16: U = x . W1(t), the pre-activation
+ *   v_t       [T, n] bf16: V = x . W3(t) for SWIGLU/BILINEAR, must be NULL otherwise
+ *   y_t       [T, d] out_dtype (BF16 or F32): the rank's partial sum
+ * U and V are rounded once from the same fp32 accumulators the activation reads.
+ * act must be GELU, SWIGLU or BILINEAR (with NONE, U is H).  Other arguments as
+ * for tp_ffn_shard_fwd; inputs are bf16.
+ * Errors: as tp_ffn_shard_fwd; TP_ERR_UNSUPPORTED for act NONE.
+ */
+int tp_ffn_shard_fwd_train(const void* x, const void* w1, const void* w3, const void* w2,
+                           void* y_t, void* h_t, void* u_t, void* v_t,
+                           int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
+                           int32_t act, int32_t out_dtype, void* hip_stream);
+
+/* Workspace of tp_ffn_shard_bwd: dU (and dV for the gated kinds), bf16 [T, n]
+ * each, every plane rounded up to 256 bytes.  0 for invalid arguments. */
+size_t tp_ffn_bwd_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t act);
+
+/*
+ * Backward of rank t's FFN share ("7.9 Tensor and pipeline parallelism",
+ * section 2.1, the f-g pattern: g, the all-reduce after the row shard, is the
+ * identity backward, so every rank receives the whole dY; f, the identity
+ * before the column shard, all-reduces the ranks' input gradients).
+ *
+ *   dy        [T, d] bf16: dL/dy for the full sublayer output
+ *   x, w1, w3, w2        as for the forward (full matrices, bf16)
+ *   h_t, u_t, v_t        what tp_ffn_shard_fwd_train kept (u_t unused and may be
+ *                        NULL for act NONE; v_t only for SWIGLU/BILINEAR)
+ *   dx_t      [T, d] dx_dtype (BF16/F32): this rank's partial input gradient
+ *             dX(t) = dU W1(t)^T [+ dV W3(t)^T]; tp_partial_sum over the ranks
+ *             gives dX (the f all-reduce)
+ *   dw2       [d_ff, d] grad_dtype (BF16/F32): rows cols(t) := H(t)^T dY
+ *   dw1, dw3  [d, d_ff] grad_dtype: columns cols(t) := X^T dU, X^T dV (dw3 only
+ *             for SWIGLU/BILINEAR, NULL otherwise)
+ *   workspace >= tp_ffn_bwd_workspace_bytes(T, d_ff, T_p, act); receives dU [, dV]
+ * with dH = dY W2(t)^T and (dU, dV) its image through the activation's
+ * derivative: GELU dU = dH gelu'(U); SWIGLU dU = dH V silu'(U), dV = dH silu(U);
+ * BILINEAR dU = dH V, dV = dH U; NONE dU = dH.
+ * The weight-gradient blocks are overwritten (not accumulated); entries outside
+ * rank t's blocks are not touched.  With T = 0 the blocks are set to zero.
+ * Four kernels are enqueued (dU, dW2, dX, dW1 [+ dW3 in the same launch]).
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_NOT_DIVISIBLE, TP_ERR_WORKSPACE,
+ * TP_ERR_UNSUPPORTED (dtype, shapes not multiples of 8), TP_ERR_HIP.
+ */
+int tp_ffn_shard_bwd(const void* x, const void* w1, const void* w3, const void* w2,
+                     const void* dy, const void* h_t, const void* u_t, const void* v_t,
+                     void* dx_t, void* dw1, void* dw3, void* dw2,
+                     void* workspace, size_t workspace_bytes,
+                     int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t, int32_t act,
+                     int32_t dx_dtype, int32_t grad_dtype, void* hip_stream);
 
 /*
  * Row-sharded attention output projection of rank t: y_t = o_t . Wo[rows(t), :].

@@ -210,6 +210,174 @@ int tp_ffn_row_fwd(const void* h_t, const void* w2, void* y_t, int64_t T, int64_
                     (hipStream_t)hip_stream);
 }
 
+int tp_ffn_shard_fwd_train(const void* x, const void* w1, const void* w3, const void* w2, void* y_t,
+                           void* h_t, void* u_t, void* v_t, int64_t T, int64_t d, int64_t d_ff,
+                           int32_t T_p, int32_t t, int32_t act, int32_t out_dtype, void* hip_stream) {
+  const char* fn = "tp_ffn_shard_fwd_train";
+  if (!h_t) return fail(TP_ERR_INVALID_ARG, "%s: h_t is NULL", fn);
+  TRY(check_ffn(fn, x, w1, w3, w2, h_t, y_t, T, d, d_ff, T_p, t, act, TP_BF16, out_dtype, true, true));
+  if (act == TP_ACT_NONE)
+    return fail(TP_ERR_UNSUPPORTED, "%s: act NONE has no pre-activation to keep (U = H)", fn);
+  const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
+  TRY(check_ptr(u_t, "u_t"));
+  if (gated) TRY(check_ptr(v_t, "v_t"));
+  else if (v_t) return fail(TP_ERR_INVALID_ARG, "%s: v_t given for a non-gated activation", fn);
+  if (T == 0) return TP_OK;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const int64_t n = d_ff / T_p;
+  // H(t) = act(X W1(t) [, X W3(t)]) with U (and V) stored from the same accumulators
+  tpk::GemmDesc g{};
+  g.A = x;
+  g.B0 = (const __bf16*)w1 + (size_t)t * n;
+  g.B1 = gated ? (const __bf16*)w3 + (size_t)t * n : nullptr;
+  g.C = h_t;
+  g.M = T;
+  g.N = (int32_t)n;
+  g.K = (int32_t)d;
+  g.lda = (int32_t)d;
+  g.ldb = (int32_t)d_ff;
+  g.ldc = (int32_t)n;
+  g.act = act;
+  g.out_f32 = false;
+  g.U = u_t;
+  g.V = gated ? v_t : nullptr;
+  g.ldu = (int32_t)n;
+  TRY(hip_status(tpk::launch_gemm_bf16(g, s), "column-parallel GEMM launch"));
+  return launch_row(h_t, w2, y_t, T, d, d_ff, T_p, t, true, out_dtype == TP_F32, s);
+}
+
+size_t tp_ffn_bwd_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t act) {
+  if (T < 0 || d_ff <= 0 || T_p < 1 || d_ff % T_p) return 0;
+  if (act < TP_ACT_NONE || act > TP_ACT_BILINEAR) return 0;
+  const size_t plane = round256((size_t)T * (size_t)(d_ff / T_p) * 2);
+  return act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR ? 2 * plane : plane;
+}
+
+int tp_ffn_shard_bwd(const void* x, const void* w1, const void* w3, const void* w2, const void* dy,
+                     const void* h_t, const void* u_t, const void* v_t, void* dx_t, void* dw1,
+                     void* dw3, void* dw2, void* workspace, size_t workspace_bytes, int64_t T,
+                     int64_t d, int64_t d_ff, int32_t T_p, int32_t t, int32_t act, int32_t dx_dtype,
+                     int32_t grad_dtype, void* hip_stream) {
+  const char* fn = "tp_ffn_shard_bwd";
+  if (!dx_t) return fail(TP_ERR_INVALID_ARG, "%s: dx_t is NULL", fn);
+  TRY(check_ffn(fn, x, w1, w3, w2, nullptr, dx_t, T, d, d_ff, T_p, t, act, TP_BF16, dx_dtype, true, true));
+  if (grad_dtype != TP_BF16 && grad_dtype != TP_F32)
+    return fail(TP_ERR_UNSUPPORTED, "%s: grad_dtype %d not supported", fn, grad_dtype);
+  const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
+  TRY(check_ptr(dy, "dy"));
+  TRY(check_ptr(h_t, "h_t"));
+  TRY(check_ptr(dw1, "dw1"));
+  TRY(check_ptr(dw2, "dw2"));
+  if (act != TP_ACT_NONE) TRY(check_ptr(u_t, "u_t"));
+  if (gated) {
+    TRY(check_ptr(v_t, "v_t"));
+    TRY(check_ptr(dw3, "dw3"));
+  } else if (v_t || dw3) {
+    return fail(TP_ERR_INVALID_ARG, "%s: v_t / dw3 given for a non-gated activation", fn);
+  }
+  const size_t need = tp_ffn_bwd_workspace_bytes(T, d_ff, T_p, act);
+  if (T > 0) {
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+    if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  const int64_t n = d_ff / T_p;
+  const size_t b = (size_t)t * n;   // first hidden unit of rank t
+  const bool gf32 = grad_dtype == TP_F32;
+  const size_t gelt = gf32 ? 4 : 2;
+  void* du = workspace;
+  void* dv = gated ? (char*)workspace + need / 2 : nullptr;
+
+  if (T > 0) {
+    // dU [, dV] = act'(dH) with dH = dY W2(t)^T: W2's row block [n, d] is B^T
+    tpk::GemmDesc g{};
+    g.A = dy;
+    g.B0 = (const __bf16*)w2 + b * (size_t)d;
+    g.C = du;
+    g.M = T;
+    g.N = (int32_t)n;
+    g.K = (int32_t)d;
+    g.lda = (int32_t)d;
+    g.ldb = (int32_t)d;
+    g.ldc = (int32_t)n;
+    g.act = act;
+    g.out_f32 = false;
+    g.U = const_cast<void*>(u_t);
+    g.V = const_cast<void*>(v_t);
+    g.dV = dv;
+    g.ldu = (int32_t)n;
+    TRY(hip_status(tpk::launch_gemm_bf16_nt(g, s), "dH GEMM launch"));
+  }
+  {
+    // dW2[cols(t), :] = H(t)^T dY: H [T, n] is A^T
+    tpk::GemmDesc g{};
+    g.A = h_t;
+    g.B0 = dy;
+    g.C = (char*)dw2 + b * (size_t)d * gelt;
+    g.M = n;
+    g.N = (int32_t)d;
+    g.K = (int32_t)T;
+    g.lda = (int32_t)n;
+    g.ldb = (int32_t)d;
+    g.ldc = (int32_t)d;
+    g.act = TP_ACT_NONE;
+    g.out_f32 = gf32;
+    TRY(hip_status(tpk::launch_gemm_bf16_tn(g, s), "dW2 GEMM launch"));
+  }
+  if (T > 0) {
+    // dX(t) = dU W1(t)^T [+ dV W3(t)^T]: W1's column block is B^T [d, n] at stride d_ff
+    tpk::GemmDesc g{};
+    g.A = du;
+    g.B0 = (const __bf16*)w1 + b;
+    g.C = dx_t;
+    g.M = T;
+    g.N = (int32_t)d;
+    g.K = (int32_t)n;
+    g.lda = (int32_t)n;
+    g.ldb = (int32_t)d_ff;
+    g.ldc = (int32_t)d;
+    g.act = TP_ACT_NONE;
+    g.out_f32 = dx_dtype == TP_F32;
+    if (gated) {
+      g.A2 = dv;
+      g.B2 = (const __bf16*)w3 + b;
+      g.K2 = (int32_t)n;
+    }
+    TRY(hip_status(tpk::launch_gemm_bf16_nt(g, s), "dX GEMM launch"));
+  }
+  {
+    // dW1[:, cols(t)] = X^T dU [, dW3[:, cols(t)] = X^T dV]: X [T, d] is A^T
+    tpk::GemmDesc g{};
+    g.A = x;
+    g.B0 = du;
+    g.C = (char*)dw1 + b * gelt;
+    g.M = d;
+    g.N = (int32_t)n;
+    g.K = (int32_t)T;
+    g.lda = (int32_t)d;
+    g.ldb = (int32_t)n;
+    g.ldc = (int32_t)d_ff;
+    g.act = TP_ACT_NONE;
+    g.out_f32 = gf32;
+    if (gated) {
+      g.nseg = 2;
+      g.Bx[0] = dv;
+      g.Cx[0] = (char*)dw3 + b * gelt;
+      g.Nx[0] = (int32_t)n;
+      g.ldbx[0] = (int32_t)n;
+      g.ldcx[0] = (int32_t)d_ff;
+    }
+    if (T == 0) {   // k = 0: nothing is read (the workspace may be absent), the blocks are zero
+      g.B0 = dw1;
+      if (gated) g.Bx[0] = dw1;
+    }
+    TRY(hip_status(tpk::launch_gemm_bf16_tn(g, s), "dW1 GEMM launch"));
+  }
+  return TP_OK;
+}
+
 int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t, int64_t T, int64_t d,
                               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t T_p,
                               int32_t t, int32_t in_dtype, int32_t out_dtype, void* hip_stream) {

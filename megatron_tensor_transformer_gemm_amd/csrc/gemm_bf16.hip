@@ -78,6 +78,36 @@ __device__ __forceinline__ float epilogue(float u, float v) {
   else return u;
 }
 
+// dU (and dV) from dH and the pre-activations u, v: the chain rule through the activation.
+__device__ __forceinline__ float gelu_grad(float u) {
+  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) +
+         u * 0.39894228040143268f * expf(-0.5f * u * u);
+}
+template <int ACT>
+__device__ __forceinline__ void act_backward(float dh, float u, float v, float& du, float& dv) {
+  if constexpr (ACT == kActGelu) {
+    du = dh * gelu_grad(u);
+    dv = 0.0f;
+  } else if constexpr (ACT == kActSwiglu) {
+    const float sg = 1.0f / (1.0f + expf(-u));
+    du = dh * v * sg * (1.0f + u * (1.0f - sg));
+    dv = dh * u * sg;
+  } else if constexpr (ACT == kActBilinear) {
+    du = dh * v;
+    dv = dh * u;
+  } else {
+    du = dh;
+    dv = 0.0f;
+  }
+}
+
+// Operand layouts.  kNN: A [M, K] and B [K, N] (the forward products).  kNT: B given as
+// B^T [N, K], both operands k-contiguous (dH = dY W2^T, dX = dU W1^T).  kTN: A given as
+// A^T [K, M], both operands m/n-contiguous (dW = X^T dU, H^T dY).  A k-contiguous operand
+// is staged as [rows][BK] and read with ds_read_b128; an m/n-contiguous one as [BK][cols]
+// and read with ds_read_b64_tr_b16, which transposes on the way to the registers.
+enum Layout : int { kNN = 0, kNT = 1, kTN = 2 };
+
 // Physical chunk of logical chunk c in A row r (ACPR 16-byte chunks per row) is
 // c ^ swz_a<ACPR>(r): 16 consecutive rows read at one logical chunk land on 16 distinct
 // 4-bank groups, and 8 consecutive rows on 8 distinct groups.
@@ -91,8 +121,12 @@ __device__ __forceinline__ int swz_a(int r) {
 // early: the wait and barrier for stage k+1 happen before the last substep of stage k, so
 // the next stage's first fragments are read, and the copies of stage k+NST are issued into
 // stage k's (now free) buffer, while that last substep multiplies.
-template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32>
+template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32, int LAYOUT, bool SAVE>
 __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int tiles_m, int tiles_n) {
+  constexpr bool A_KC = LAYOUT != kTN;        // A tile [BM][BK] (else [BK][BM])
+  constexpr bool B_KC = LAYOUT == kNT;        // B tile [BN][BK] (else [BK][BN])
+  static_assert(!DUAL || LAYOUT == kNN, "gated pair only in the forward layout");
+  static_assert(!SAVE || (LAYOUT == kNN && !OUT_F32), "pre-activations are kept by the forward");
   constexpr int NSUB = DUAL ? 2 : 1;          // B sub-tiles: W1 block | W3 block
   constexpr int BNS = BN / NSUB;              // B columns per sub-tile = output tile width
   constexpr int WTM = BM / 2;                 // rows per wave (2 x 2 waves)
@@ -111,10 +145,12 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   constexpr int B_LD = NSUB * SUB_BYTES / 1024 / 4;
   constexpr int LPS = A_LD + B_LD;            // copies per wave per stage
   constexpr int QSUB = SUB_BYTES / 1024;      // copies per sub-tile
-  constexpr int CPR = BNS / 8;                // 16-byte chunks per B row
-  constexpr int PITCH = BNS * 2;              // bytes per B row
+  constexpr int CPR = BNS / 8;                // 16-byte chunks per B row ([BK][BN] tile)
+  constexpr int PITCH = BNS * 2;              // bytes per B row ([BK][BN] tile)
+  constexpr int MCPR = BM / 8;                // 16-byte chunks per A row ([BK][BM] tile)
+  constexpr int MPITCH = BM * 2;              // bytes per A row ([BK][BM] tile)
   static_assert(MB >= 1 && NBS >= 1 && A_LD >= 1 && B_LD >= 1, "tile too small");
-  static_assert(CPR >= 8, "B sub-tile narrower than 64 columns");
+  static_assert(CPR >= 8 && MCPR >= 8, "tile narrower than 64 columns");
   static_assert(KSUB % 2 == 0 && (ACPR == 4 || ACPR == 8), "BK must be 32 or 64");
   static_assert(NST >= 2 && NST <= 5 && (NST - 1) * LPS <= 63, "stages");
 
@@ -163,22 +199,38 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   const int64_t rows_left64 = g.M - m0;
   const int rows_left = rows_left64 < BM ? (int)rows_left64 : BM;
 
-  const __bf16* A = (const __bf16*)g.A + m0 * g.lda;
-  const __bf16* B0 = (const __bf16*)Bseg + n0;
+  // Tile origins; a k-tile then advances by k0 (k-contiguous) or k0 rows (m/n-contiguous).
+  const int64_t a_org = A_KC ? m0 * g.lda : m0;
+  const int64_t b_org = B_KC ? (int64_t)n0 * ldb_ : n0;
+  const __bf16* A = (const __bf16*)g.A + a_org;
+  const __bf16* B0 = (const __bf16*)Bseg + b_org;
   const __bf16* B1 = DUAL ? (const __bf16*)g.B1 + n0 : B0;
+  // second k segment (kNT): same origins in A2/B2
+  const __bf16* A2 = LAYOUT == kNT && g.A2 ? (const __bf16*)g.A2 + a_org : A;
+  const __bf16* B2 = LAYOUT == kNT && g.B2 ? (const __bf16*)g.B2 + b_org : B0;
+  const int nk0 = LAYOUT == kNT ? (g.K + BK - 1) / BK : 0x7FFFFFFF;
 
   // ---- per-lane global->LDS descriptors (fixed over the k loop).  Lanes whose row (A)
   // or column (B) lies outside the matrix get an out-of-range offset once and for all;
   // the k-tail is masked only in the last, partial k-tile.
+  // a_kc / b_kr: the k of the copied chunk (k-contiguous) or of the copied row.
   uint32_t a_voff[A_LD];
   int a_kc[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = wave * A_LD + i;
-    const int row = q * ARPI + lane / ACPR;
-    const int c = (lane % ACPR) ^ swz_a<ACPR>(row);
-    a_voff[i] = row < rows_left ? (uint32_t)(row * g.lda + 8 * c) * 2u : kOOB;
-    a_kc[i] = 8 * c;
+    if constexpr (A_KC) {
+      const int row = q * ARPI + lane / ACPR;
+      const int c = (lane % ACPR) ^ swz_a<ACPR>(row);
+      a_voff[i] = row < rows_left ? (uint32_t)(row * g.lda + 8 * c) * 2u : kOOB;
+      a_kc[i] = 8 * c;
+    } else {
+      const int pos = q * 64 + lane;
+      const int row = pos / MCPR;
+      const int c = (pos % MCPR) ^ (swz_b(row) & (MCPR - 1));
+      a_voff[i] = 8 * c < rows_left ? (uint32_t)(row * g.lda + 8 * c) * 2u : kOOB;
+      a_kc[i] = row;
+    }
   }
   uint32_t b_voff[B_LD];
   int b_kr[B_LD];
@@ -186,52 +238,90 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   for (int i = 0; i < B_LD; ++i) {
     const int q = wave * B_LD + i;
     const int pos = (q % QSUB) * 64 + lane;
-    const int row = pos / CPR;
-    const int c = (pos % CPR) ^ (swz_b(row) & (CPR - 1));
-    b_voff[i] = (n0 + 8 * c < N_) ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
-    b_kr[i] = row;
+    if constexpr (B_KC) {
+      const int row = pos / ACPR;
+      const int c = (pos % ACPR) ^ swz_a<ACPR>(row);
+      b_voff[i] = n0 + row < N_ ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
+      b_kr[i] = 8 * c;
+    } else {
+      const int row = pos / CPR;
+      const int c = (pos % CPR) ^ (swz_b(row) & (CPR - 1));
+      b_voff[i] = (n0 + 8 * c < N_) ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
+      b_kr[i] = row;
+    }
   }
   // B sub-tile a wave's copies land in is the same for all of its copies.
   const bool b_second = (wave * B_LD) / QSUB != 0;
 
   auto issue = [&](int kt, LDS_AS unsigned char* base) {
-    const int k0 = kt * BK;
-    const bool full = k0 + BK <= g.K;
-    const i32x4 da = make_desc(A + k0);
-    const i32x4 db = make_desc((b_second ? B1 : B0) + (int64_t)k0 * ldb_);
+    int k0 = kt * BK;
+    int Kc = g.K;
+    const __bf16* Ab = A;
+    const __bf16* Bb = b_second ? B1 : B0;
+    if constexpr (LAYOUT == kNT) {
+      if (kt >= nk0) {   // second k segment (past its end every copy is masked)
+        k0 -= nk0 * BK;
+        Kc = g.K2;
+        Ab = A2;
+        Bb = B2;
+      }
+    }
+    const bool full = k0 + BK <= Kc;
+    const i32x4 da = make_desc(Ab + (A_KC ? (int64_t)k0 : (int64_t)k0 * g.lda));
+    const i32x4 db = make_desc(Bb + (B_KC ? (int64_t)k0 : (int64_t)k0 * ldb_));
     const uint32_t lds = (uint32_t)(uintptr_t)base;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const uint32_t v = (full || k0 + a_kc[i] < g.K) ? a_voff[i] : kOOB;
+      const uint32_t v = (full || k0 + a_kc[i] < Kc) ? a_voff[i] : kOOB;
       copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (wave * A_LD + i) * 1024));
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const uint32_t v = (full || k0 + b_kr[i] < g.K) ? b_voff[i] : kOOB;
+      const uint32_t v = (full || k0 + b_kr[i] < Kc) ? b_voff[i] : kOOB;
       copy16_to_lds(db, v,
                     __builtin_amdgcn_readfirstlane(lds + A_BYTES + (wave * B_LD + i) * 1024));
     }
   };
 
   // ---- per-lane LDS read offsets
+  // k-contiguous tiles: row r of the fragment at lane r % 32, chunk 2*s + lane / 32.
+  // m/n-contiguous tiles: 16-lane group g4 reads 4 k-rows x 16 columns per transposing read.
   const int arow = wm * WTM + (lane & 31);
-  uint32_t a_rd[KSUB];
-#pragma unroll
-  for (int s = 0; s < KSUB; ++s) {
-    const int c = 2 * s + (lane >> 5);
-    a_rd[s] = (uint32_t)(arow * AROWB + ((c ^ swz_a<ACPR>(arow)) << 4));
-  }
+  uint32_t a_rd[A_KC ? KSUB : MB];
   const int g4 = lane >> 4, i16 = lane & 15;
   const int krow_l = 8 * (g4 >> 1) + (i16 >> 2);
-  const int sw = swz_b(krow_l) & (CPR - 1);
-  uint32_t b_rd[NB];
+  if constexpr (A_KC) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int sub = nb / NBS;
-    const int colbase = wn * WCOLS + (nb % NBS) * 32;
-    const int n = colbase + 16 * (g4 & 1) + 4 * (i16 & 3);
-    b_rd[nb] = (uint32_t)(sub * SUB_BYTES + krow_l * PITCH + (((n >> 3) ^ sw) << 4) +
-                          ((n >> 2) & 1) * 8);
+    for (int s = 0; s < KSUB; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      a_rd[s] = (uint32_t)(arow * AROWB + ((c ^ swz_a<ACPR>(arow)) << 4));
+    }
+  } else {
+    const int swm = swz_b(krow_l) & (MCPR - 1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int n = wm * WTM + mb * 32 + 16 * (g4 & 1) + 4 * (i16 & 3);
+      a_rd[mb] = (uint32_t)(krow_l * MPITCH + (((n >> 3) ^ swm) << 4) + ((n >> 2) & 1) * 8);
+    }
+  }
+  const int sw = swz_b(krow_l) & (CPR - 1);
+  const int bcol = wn * WCOLS + (lane & 31);
+  uint32_t b_rd[B_KC ? KSUB : NB];
+  if constexpr (B_KC) {
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      b_rd[s] = (uint32_t)(bcol * AROWB + ((c ^ swz_a<ACPR>(bcol)) << 4));
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int sub = nb / NBS;
+      const int colbase = wn * WCOLS + (nb % NBS) * 32;
+      const int n = colbase + 16 * (g4 & 1) + 4 * (i16 & 3);
+      b_rd[nb] = (uint32_t)(sub * SUB_BYTES + krow_l * PITCH + (((n >> 3) ^ sw) << 4) +
+                            ((n >> 2) & 1) * 8);
+    }
   }
 
   f32x16 acc[MB][NB];
@@ -245,14 +335,26 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
                         bf16x8 (&bfr)[NB]) {
     const LDS_AS unsigned char* Bs = As + A_BYTES;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * AROWB);
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (A_KC) {
+        af[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * AROWB);
+      } else {
+        const LDS_AS unsigned char* p = As + a_rd[mb] + 16 * s * MPITCH;
+        bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+        bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * MPITCH));
+        af[mb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
-      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
-      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
-      bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (B_KC) {
+        bfr[nb] = *(const LDS_AS bf16x8*)(Bs + b_rd[s] + nb * 32 * AROWB);
+      } else {
+        const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
+        bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+        bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+        bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
   };
   auto mfmas = [&](const bf16x8 (&af)[MB], const bf16x8 (&bfr)[NB]) {
@@ -264,7 +366,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   };
   // Scheduling hint for one substep with the next substep's reads: alternate one MFMA and
   // one LDS read, then the rest.
-  constexpr int NREAD = MB + 2 * NB;  // LDS reads per substep
+  constexpr int NREAD = (A_KC ? MB : 2 * MB) + (B_KC ? NB : 2 * NB);  // LDS reads per substep
   constexpr int NMFMA = MB * NB;      // MFMAs per substep
   constexpr int NPAIR = NMFMA < NREAD ? NMFMA : NREAD;
   auto interleave = [&]() {
@@ -281,7 +383,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   bf16x8 bfr[2][NB];
   // k-tiles, padded to a multiple of NST: tiles past K load as zeros (every copy
   // out of range), so every stage runs the same branch-free product code.
-  const int nk = ((g.K + BK - 1) / BK + NST - 1) / NST * NST;
+  const int nk_all = LAYOUT == kNT ? nk0 + (g.K2 + BK - 1) / BK : (g.K + BK - 1) / BK;
+  const int nk = (nk_all + NST - 1) / NST * NST;
 
   // prologue: NST stages in flight, then stage 0's first fragments
 #pragma unroll
@@ -332,11 +435,38 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
         const int n = n0 + wn * WCOLS + nb * 32 + 8 * q + 4 * (lane >> 5);
         if (n >= N_) continue;
         float v[4];
+        if constexpr (LAYOUT == kNT && ACT != kActNone) {
+          // accumulator = dH; U [, V] saved by the forward -> dU (C) [, dV]
+          const bf16x4 uu = *(const bf16x4*)((const __bf16*)g.U + m * g.ldu + n);
+          bf16x4 vv = bf16x4{};
+          if constexpr (ACT != kActGelu) vv = *(const bf16x4*)((const __bf16*)g.V + m * g.ldu + n);
+          float dv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float u = acc[mb][nb][4 * q + e];
-          const float w = DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f;
-          v[e] = epilogue<ACT>(u, w);
+          for (int e = 0; e < 4; ++e)
+            act_backward<ACT>(acc[mb][nb][4 * q + e], (float)uu[e], (float)vv[e], v[e], dv[e]);
+          if constexpr (ACT != kActGelu)
+            *(bf16x4*)((__bf16*)g.dV + m * ldc_ + n) =
+                bf16x4{(__bf16)dv[0], (__bf16)dv[1], (__bf16)dv[2], (__bf16)dv[3]};
+        } else if constexpr (LAYOUT == kNN) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float u = acc[mb][nb][4 * q + e];
+            const float w = DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f;
+            v[e] = epilogue<ACT>(u, w);
+          }
+          if constexpr (SAVE) {   // keep the pre-activations for the backward pass
+            const f32x16& au = acc[mb][nb];
+            *(bf16x4*)((__bf16*)g.U + m * g.ldu + n) =
+                bf16x4{(__bf16)au[4 * q], (__bf16)au[4 * q + 1], (__bf16)au[4 * q + 2], (__bf16)au[4 * q + 3]};
+            if constexpr (DUAL) {
+              const f32x16& av = acc[mb][nb + NBS];
+              *(bf16x4*)((__bf16*)g.V + m * g.ldu + n) =
+                  bf16x4{(__bf16)av[4 * q], (__bf16)av[4 * q + 1], (__bf16)av[4 * q + 2], (__bf16)av[4 * q + 3]};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[mb][nb][4 * q + e];
         }
         if constexpr (OUT_F32) {
           float* c = (float*)Cseg + m * ldc_ + n;
@@ -350,14 +480,14 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   }
 }
 
-template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32>
+template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32, int LAYOUT, bool SAVE>
 hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? BN / 2 : BN;
   const int64_t tm = (g.M + BM - 1) / BM;
   int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
   for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) tn += (g.Nx[i] + OUT_BN - 1) / OUT_BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, DUAL, ACT, OUT_F32>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, DUAL, ACT, OUT_F32, LAYOUT, SAVE>),
                      dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
@@ -365,25 +495,34 @@ hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
 // Tile choice: 256x256 tiles once they give at least one full wave of workgroups over the
 // 256 CUs, else 128x128 (or 128x256 for the gated pair).  Long k-loops use 4 stages of 32 k
 // (more copies in flight); short ones 2 stages of 64 k (fewer, longer stages).
-template <bool DUAL, int ACT, bool OUT_F32>
+template <bool DUAL, int ACT, bool OUT_F32, int LAYOUT = kNN, bool SAVE = false>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
   int64_t ncols = g.N;
   for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) ncols += g.Nx[i];
   const int64_t big = ((g.M + 255) / 256) * ((ncols + OUT_BN - 1) / OUT_BN);
+  const int64_t kdepth = (int64_t)g.K + (LAYOUT == kNT ? g.K2 : 0);
   if (big >= 256) {
-    if (g.K > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32>(g, s);
-    return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32>(g, s);
+    if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+    return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
   }
-  return launch_cfg<128, DUAL ? 256 : 128, 64, 2, DUAL, ACT, OUT_F32>(g, s);
+  return launch_cfg<128, DUAL ? 256 : 128, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.out_f32) {
-    if (g.act != kActNone) return hipErrorInvalidValue;
+    if (g.act != kActNone || g.U) return hipErrorInvalidValue;
     return launch_sized<false, kActNone, true>(g, s);
+  }
+  if (g.U) {   // forward that also keeps U (and V) for the backward
+    switch (g.act) {
+      case kActGelu: return launch_sized<false, kActGelu, false, kNN, true>(g, s);
+      case kActSwiglu: return launch_sized<true, kActSwiglu, false, kNN, true>(g, s);
+      case kActBilinear: return launch_sized<true, kActBilinear, false, kNN, true>(g, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (g.act) {
     case kActNone: return launch_sized<false, kActNone, false>(g, s);
@@ -392,6 +531,26 @@ hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t s) {
     case kActBilinear: return launch_sized<true, kActBilinear, false>(g, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_bf16_nt(const GemmDesc& g, hipStream_t s) {
+  if (g.out_f32) {
+    if (g.act != kActNone) return hipErrorInvalidValue;
+    return launch_sized<false, kActNone, true, kNT>(g, s);
+  }
+  switch (g.act) {
+    case kActNone: return launch_sized<false, kActNone, false, kNT>(g, s);
+    case kActGelu: return launch_sized<false, kActGelu, false, kNT>(g, s);
+    case kActSwiglu: return launch_sized<false, kActSwiglu, false, kNT>(g, s);
+    case kActBilinear: return launch_sized<false, kActBilinear, false, kNT>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_bf16_tn(const GemmDesc& g, hipStream_t s) {
+  if (g.act != kActNone) return hipErrorInvalidValue;
+  return g.out_f32 ? launch_sized<false, kActNone, true, kTN>(g, s)
+                   : launch_sized<false, kActNone, false, kTN>(g, s);
 }
 
 }  // namespace tpk

@@ -28,10 +28,29 @@ struct GemmDesc {
   const void* Bx[2] = {nullptr, nullptr};
   void* Cx[2] = {nullptr, nullptr};
   int32_t Nx[2] = {0, 0}, ldbx[2] = {0, 0}, ldcx[2] = {0, 0};
+  // Second k segment (launch_gemm_bf16_nt): C = A.B0 + A2.B2, A2/B2 K2 deep with the
+  // same leading dimensions (dX = dU W1^T + dV W3^T in one accumulation).
+  const void* A2 = nullptr;
+  const void* B2 = nullptr;
+  int32_t K2 = 0;
+  // Pre-activations U, V [M, N] with leading dimension ldu: the forward stores them when
+  // non-null; the backward reads them and writes dU to C and dV (gated kinds) to dV.
+  void* U = nullptr;
+  void* V = nullptr;
+  void* dV = nullptr;
+  int32_t ldu = 0;
 };
 
 // bf16 inputs, fp32 accumulation on MFMA; output bf16 (or fp32 if out_f32).
+// A [M, K] and B [K, N], both row-major; the activation `act` in the epilogue.
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t s);
+// A [M, K] and B given as B^T [N, K] (rows of B^T at stride ldb); with act != none the
+// accumulator is dH and the epilogue applies the activation's derivative:
+// C = dU (bf16), dV for the gated kinds.
+hipError_t launch_gemm_bf16_nt(const GemmDesc& g, hipStream_t s);
+// A given as A^T [K, M] (stride lda) and B [K, N]: C = A.B, no activation (weight
+// gradients X^T dU, H^T dY).
+hipError_t launch_gemm_bf16_tn(const GemmDesc& g, hipStream_t s);
 // fp32 inputs and output.
 hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t s);
 

@@ -27,7 +27,7 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-T_X, T_W1, T_W3, T_W2, T_WQ, T_WK, T_WV, T_WO, T_O = range(9)
+T_X, T_W1, T_W3, T_W2, T_WQ, T_WK, T_WV, T_WO, T_O, T_DY = range(10)
 
 
 @dataclass(frozen=True)
@@ -134,7 +134,8 @@ def encode(a: np.ndarray, dtype: str) -> np.ndarray:
 def make_tensor(w: Workload, name: str) -> np.ndarray:
     """Generate one full tensor of a workload, encoded in the workload's dtype.
 
-    name in {"x", "w1", "w3", "w2", "wq", "wk", "wv", "wo", "o"}.
+    name in {"x", "w1", "w3", "w2", "wq", "wk", "wv", "wo", "o", "dy"}; "dy" is the
+    gradient of the loss with respect to the sublayer output, N(0, 1), for the backward.
     """
     if name == "x":
         a = draw(w.cid, T_X, (w.T, w.d), w.x_std)
@@ -162,6 +163,8 @@ def make_tensor(w: Workload, name: str) -> np.ndarray:
         if not w.has_attn_outproj:
             raise ValueError(f"{w.name} has no synthetic head outputs")
         a = draw(w.cid, T_O, (w.T, w.n_heads * w.head_dim), 1.0)
+    elif name == "dy":
+        a = draw(w.cid, T_DY, (w.T, w.d), 1.0)
     else:
         raise KeyError(name)
     return encode(a, w.dtype)
@@ -172,7 +175,8 @@ def small_ffn_case(seed: int, T: int, d: int, d_ff: int, act: str, dtype: str,
                    w2_std: float | None = None) -> dict:
     """Seeded small/ragged FFN inputs for parity and edge-case tests.
 
-    Returns encoded x [T,d], w1/w3 [d,d_ff], w2 [d_ff,d] (w3 only for swiglu).
+    Returns encoded x [T,d], w1/w3 [d,d_ff], w2 [d_ff,d] (w3 only for the gated kinds)
+    and dy [T,d] (N(0,1), the output gradient for the backward).
     Default stds are 1/sqrt(fan_in) of the full matrices.
     """
     w1_std = 1.0 / math.sqrt(d) if w1_std is None else w1_std
@@ -183,8 +187,9 @@ def small_ffn_case(seed: int, T: int, d: int, d_ff: int, act: str, dtype: str,
         "w1": encode(draw(cid, T_W1, (d, d_ff), w1_std), dtype),
         "w2": encode(draw(cid, T_W2, (d_ff, d), w2_std), dtype),
     }
-    if act == "swiglu":
+    if act in ("swiglu", "bilinear"):
         out["w3"] = encode(draw(cid, T_W3, (d, d_ff), w1_std), dtype)
+    out["dy"] = encode(draw(cid, T_DY, (T, d), 1.0), dtype)
     return out
 
 
@@ -208,3 +213,29 @@ def integer_offset_case(T: int, d: int, d_ff: int, seed: int = 7) -> dict:
     w3[(5 * cols + 3) % d, cols] = g.choice([-1.0, 1.0], size=d_ff)
     w2 = g.integers(-1, 2, size=(d_ff, d)).astype(np.float32)
     return {"x": bf16_bits(x), "w1": bf16_bits(w1), "w3": bf16_bits(w3), "w2": bf16_bits(w2)}
+
+
+def integer_backward_case(T: int, d: int, d_ff: int, seed: int = 7) -> dict:
+    """Integer-valued inputs whose sharded FFN backward is exact (activation NONE or
+    BILINEAR, float32 gradients).
+
+    x: integers in [-8, 8]; W1 and W3 as in integer_offset_case (one +-1 per
+    column, so U and V are signed copies of x columns, |U|, |V| <= 8).  W2: one
+    +-1 per row (hidden unit j) at column (3*j + 1) mod d, so dH = dY W2(t)^T is a
+    signed copy of dY columns.  dy: integers in [-4, 4].  Then |dU|, |dV| <= 32 and
+    |H| <= 64 (exact in bf16) and every gradient entry is an integer below 2^24 for
+    T < 65536: any summation order gives the same bits, and a wrong block offset
+    shows up as different integers.  Returned as bf16 bit patterns.
+    """
+    g = np.random.Generator(np.random.PCG64(525252 + seed))
+    x = g.integers(-8, 9, size=(T, d)).astype(np.float32)
+    w1 = np.zeros((d, d_ff), dtype=np.float32)
+    w3 = np.zeros((d, d_ff), dtype=np.float32)
+    w2 = np.zeros((d_ff, d), dtype=np.float32)
+    cols = np.arange(d_ff)
+    w1[(7 * cols) % d, cols] = g.choice([-1.0, 1.0], size=d_ff)
+    w3[(5 * cols + 3) % d, cols] = g.choice([-1.0, 1.0], size=d_ff)
+    w2[cols, (3 * cols + 1) % d] = g.choice([-1.0, 1.0], size=d_ff)
+    dy = g.integers(-4, 5, size=(T, d)).astype(np.float32)
+    return {"x": bf16_bits(x), "w1": bf16_bits(w1), "w3": bf16_bits(w3), "w2": bf16_bits(w2),
+            "dy": bf16_bits(dy)}

@@ -51,6 +51,11 @@ _SIGS = {
     "tp_attn_core_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                 _i32, _vp]),
     "tp_partial_sum": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "tp_ffn_shard_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
+                                      _i32, _i32, _i32, _vp]),
+    "tp_ffn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "tp_ffn_shard_bwd": (_i32, [_vp] * 12 + [_vp, _sz, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                             _vp]),
 }
 
 _lib = None
@@ -183,6 +188,31 @@ def tp_partial_sum(partials, partial_stride, T_p, residual, y, n_elems, part_dty
     _check("tp_partial_sum", lib().tp_partial_sum(
         _ptr(partials), partial_stride, T_p, _ptr(residual), _ptr(y), n_elems, part_dtype,
         out_dtype, _stream(hip_stream)))
+
+
+def tp_ffn_shard_fwd_train(x, w1, w3, w2, y_t, h_t, u_t, v_t, T, d, d_ff, T_p, t, act, out_dtype,
+                           hip_stream=None):
+    if isinstance(act, str):
+        act = ACT[act]
+    _check("tp_ffn_shard_fwd_train", lib().tp_ffn_shard_fwd_train(
+        _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y_t), _ptr(h_t), _ptr(u_t), _ptr(v_t), T, d, d_ff,
+        T_p, t, act, out_dtype, _stream(hip_stream)))
+
+
+def tp_ffn_bwd_workspace_bytes(T: int, d_ff: int, T_p: int, act) -> int:
+    if isinstance(act, str):
+        act = ACT[act]
+    return lib().tp_ffn_bwd_workspace_bytes(T, d_ff, T_p, act)
+
+
+def tp_ffn_shard_bwd(x, w1, w3, w2, dy, h_t, u_t, v_t, dx_t, dw1, dw3, dw2, workspace,
+                     workspace_bytes, T, d, d_ff, T_p, t, act, dx_dtype, grad_dtype, hip_stream=None):
+    if isinstance(act, str):
+        act = ACT[act]
+    _check("tp_ffn_shard_bwd", lib().tp_ffn_shard_bwd(
+        _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(dy), _ptr(h_t), _ptr(u_t), _ptr(v_t), _ptr(dx_t),
+        _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(workspace), workspace_bytes, T, d, d_ff, T_p, t, act,
+        dx_dtype, grad_dtype, _stream(hip_stream)))
 
 
 # ----------------------------------------------------------------------------- tensor helpers

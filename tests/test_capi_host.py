@@ -22,10 +22,10 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
-    assert S.tp_abi_version() == 1
+    assert S.tp_abi_version() == 2
 
 
 @pytest.mark.parametrize("extent,T_p", [(14336, 8), (28672, 8), (4096, 4), (27720, 11), (0, 3),
@@ -139,4 +139,55 @@ def test_attn_core_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_attn_core_fwd(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+def test_backward_workspace_query():
+    assert S.tp_ffn_bwd_workspace_bytes(8192, 14336, 8, "swiglu") == 2 * 8192 * 1792 * 2
+    assert S.tp_ffn_bwd_workspace_bytes(8192, 14336, 8, "gelu") == 8192 * 1792 * 2
+    assert S.tp_ffn_bwd_workspace_bytes(3, 24, 8, "swiglu") == 2 * 256      # each plane rounded up
+    assert S.tp_ffn_bwd_workspace_bytes(64, 1000, 3, "gelu") == 0
+    assert S.tp_ffn_bwd_workspace_bytes(64, 1024, 2, 9) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(act=S.TP_ACT_NONE), S.TP_ERR_UNSUPPORTED),             # U would be H
+    (dict(u_t=None), S.TP_ERR_INVALID_ARG),
+    (dict(v_t=P), S.TP_ERR_INVALID_ARG),                          # V with GELU
+    (dict(act=S.TP_ACT_SWIGLU, w3=P), S.TP_ERR_INVALID_ARG),      # SwiGLU without v_t
+    (dict(h_t=None), S.TP_ERR_INVALID_ARG),
+    (dict(out_dtype=7), S.TP_ERR_UNSUPPORTED),
+    (dict(d_ff=1000, T_p=3), S.TP_ERR_NOT_DIVISIBLE),
+])
+def test_train_forward_rejects_before_launch(kw, code):
+    a = dict(x=P, w1=P, w3=None, w2=P, y_t=P, h_t=P, u_t=P, v_t=None, T=64, d=256, d_ff=1024, T_p=2,
+             t=0, act=S.TP_ACT_GELU, out_dtype=S.TP_BF16, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_ffn_shard_fwd_train(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), S.TP_ERR_INVALID_ARG),
+    (dict(dx_t=None), S.TP_ERR_INVALID_ARG),
+    (dict(dw2=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(u_t=None), S.TP_ERR_INVALID_ARG),                       # GELU needs U
+    (dict(dw3=P), S.TP_ERR_INVALID_ARG),                          # dW3 with GELU
+    (dict(act=S.TP_ACT_SWIGLU, w3=P, dw3=P), S.TP_ERR_INVALID_ARG),   # SwiGLU without v_t
+    (dict(act=S.TP_ACT_SWIGLU, w3=P, v_t=P), S.TP_ERR_INVALID_ARG),   # SwiGLU without dw3
+    (dict(grad_dtype=3), S.TP_ERR_UNSUPPORTED),
+    (dict(dx_dtype=3), S.TP_ERR_UNSUPPORTED),
+    (dict(d=260), S.TP_ERR_UNSUPPORTED),
+    (dict(workspace_bytes=100), S.TP_ERR_WORKSPACE),
+    (dict(workspace=None), S.TP_ERR_WORKSPACE),
+    (dict(t=2), S.TP_ERR_INVALID_ARG),
+])
+def test_backward_rejects_before_launch(kw, code):
+    a = dict(x=P, w1=P, w3=None, w2=P, dy=P, h_t=P, u_t=P, v_t=None, dx_t=P, dw1=P, dw3=None, dw2=P,
+             workspace=P, workspace_bytes=1 << 30, T=64, d=256, d_ff=1024, T_p=2, t=0,
+             act=S.TP_ACT_GELU, dx_dtype=S.TP_BF16, grad_dtype=S.TP_F32, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_ffn_shard_bwd(**a)
     assert e.value.code == code, S.tp_last_error()

@@ -2,6 +2,8 @@
 the local partial sum, against the CPU oracle, through the C ABI."""
 from __future__ import annotations
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -67,7 +69,7 @@ CASES = [
 def test_ffn_shard_parity_small(case):
     T, d, d_ff, T_p, act, dt, odt = case
     log(f"[ffn] {case}")
-    c = I.small_ffn_case(hash(case) % 1000, T, d, d_ff, act, dt)
+    c = I.small_ffn_case(zlib.crc32(repr(case).encode()) % 1000, T, d, d_ff, act, dt)
     code = S.TP_BF16 if dt == I.BF16 else S.TP_F32
     ocode = S.TP_BF16 if odt == I.BF16 else S.TP_F32
     xd, w1d, w2d = dev(c["x"], dt), dev(c["w1"], dt), dev(c["w2"], dt)

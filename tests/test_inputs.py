@@ -65,3 +65,22 @@ def test_integer_case_is_exact():
     assert np.all(x == np.round(x)) and np.max(np.abs(x)) <= 8
     w1 = I.bf16_to_f32(c["w1"])
     assert np.all(np.sum(np.abs(w1), axis=0) == 1)
+
+
+def test_integer_backward_case_is_exact_in_the_kernels_formats():
+    """The integer backward case keeps dU, dV within +-32 and H within +-64 (bf16-exact
+    integers) and every gradient an integer below 2^24 (fp32-exact)."""
+    from oracle import tp_oracle as O
+    c = I.integer_backward_case(300, 264, 544)
+    x, w1, w3, w2, dy = (I.as_f64(c[k], I.BF16) for k in ("x", "w1", "w3", "w2", "dy"))
+    for act in ("none", "bilinear"):
+        for t in range(4):
+            r = O.ffn_shard_bwd(x, w1, w3, w2, dy, 4, t, act)
+            for k in ("du", "dv", "h", "dx_t", "dw1", "dw2", "dw3"):
+                a = r[k]
+                if a is None:
+                    continue
+                assert np.all(a == np.round(a)) and np.max(np.abs(a)) < 2 ** 24, k
+            assert np.max(np.abs(r["du"])) <= 32 and np.max(np.abs(r["h"])) <= 64
+            if r["dv"] is not None:
+                assert np.max(np.abs(r["dv"])) <= 32
