@@ -80,6 +80,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the extra GPT-style block measurement (attention core)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the extra measurement of the FFN shard backward")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="read the rocprofv3 counter_collection.csv files of two --pmc-pass "
                          "runs (FETCH_SIZE, WRITE_SIZE), write profiles/hbm_traffic.json, exit")
@@ -262,6 +264,8 @@ def main() -> int:
         "roofline": roofline,
     }
 
+    if not args.no_backward:
+        out["backward"] = measure_backward(w, X, W1, W3, W2, max(2, args.steps // 4), 1)
     if not args.no_block:
         out["block_workload"] = measure_block(max(2, args.steps // 4), 1)
     if not args.no_cpu_baseline:
@@ -311,6 +315,82 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
         json.dump(out, f, indent=1)
     print(json.dumps(out["kernels"], indent=1))
     return 0
+
+
+def measure_backward(w, X, W1, W3, W2, steps: int, warmup: int) -> dict:
+    """Backward of the FFN sublayer's TP shards at the headline shape, all ranks: per rank
+    tp_ffn_shard_bwd (dU/dV with the SwiGLU derivative, dW2, dX(t), dW1|dW3), then the
+    partial sum of the ranks' dX(t) (the f all-reduce).  The ranks' saved activations (H, U,
+    V from the training forward) are made before the timed region.  Algorithmic FLOPs per
+    rank: 2*T*d*n for dH, dW2 each, 4*T*d*n for dX and for dW1|dW3 (gated)."""
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from megatron_tensor_transformer_gemm_amd import tpshard as S
+
+    torch.cuda.empty_cache()
+    T, d, d_ff, T_p = w.T, w.d, w.d_ff, w.T_p
+    n = d_ff // T_p
+    BF, F32 = S.TP_BF16, S.TP_F32
+    log(f"[bench] backward {w.name}: saved activations of {T_p} ranks")
+    dy = torch.from_numpy(np.ascontiguousarray(I.make_tensor(w, "dy")).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    saved = []
+    yt = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    for t in range(T_p):
+        h, u, v = (torch.empty((T, n), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+        S.tp_ffn_shard_fwd_train(X, W1, W3, W2, yt, h, u, v, T, d, d_ff, T_p, t, S.TP_ACT_SWIGLU, BF)
+        saved.append((h, u, v))
+    del yt
+    dW1 = torch.empty((d, d_ff), dtype=torch.float32, device="cuda")
+    dW3 = torch.empty((d, d_ff), dtype=torch.float32, device="cuda")
+    dW2 = torch.empty((d_ff, d), dtype=torch.float32, device="cuda")
+    stride = T * d + PSUM_PAD
+    Pf = torch.empty(T_p * stride, dtype=torch.bfloat16, device="cuda")
+    P = [Pf[t * stride: t * stride + T * d].view(T, d) for t in range(T_p)]
+    dX = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    nb = S.tp_ffn_bwd_workspace_bytes(T, d_ff, T_p, S.TP_ACT_SWIGLU)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        for t in range(T_p):
+            h, u, v = saved[t]
+            S.tp_ffn_shard_bwd(X, W1, W3, W2, dy, h, u, v, P[t], dW1, dW3, dW2, ws, nb, T, d, d_ff,
+                               T_p, t, S.TP_ACT_SWIGLU, BF, F32)
+            if evs:
+                evs[t + 1].record()
+        S.tp_partial_sum(Pf, stride, T_p, None, dX, T * d, BF, BF)
+        if evs:
+            evs[T_p + 1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(T_p + 2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    rank_us = 1e3 * sum(e[t].elapsed_time(e[t + 1]) for e in ev for t in range(T_p)) / (steps * T_p)
+    psum_us = 1e3 * sum(e[T_p].elapsed_time(e[T_p + 1]) for e in ev) / steps
+    fl_rank = 12.0 * T * d * n
+    res = {"workload": f"{w.name} backward: {T_p} ranks' tp_ffn_shard_bwd + partial sum of dX",
+           "ms_per_step": round(ms, 3),
+           "tflops": round(T_p * fl_rank / (ms * 1e-3) / 1e12, 1),
+           "frac_of_peak": round(T_p * fl_rank / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "per_rank_us": round(rank_us, 1),
+           "per_rank_tflops": round(fl_rank / (rank_us * 1e-6) / 1e12, 1),
+           "flops_per_rank": fl_rank,
+           "dx_partial_sum_us": round(psum_us, 1),
+           "dtypes": {"inputs": "bf16", "dx": "bf16", "weight_grads": "f32"},
+           "steps": steps}
+    log(f"[bench] backward: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; per rank {rank_us:.1f} us")
+    return res
 
 
 def measure_block(steps: int, warmup: int) -> dict:
