@@ -264,6 +264,26 @@ def main() -> int:
         "roofline": roofline,
     }
 
+    # sequence-parallel form of the same reduce: 8 ranks' row slices (reduce-scatter)
+    rs_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rs_reps = 5
+    for _ in range(2):
+        for t in range(T_p):
+            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Y[t * (T // T_p):], T, d, BF, BF)
+    rs_ev[0].record()
+    for _ in range(rs_reps):
+        for t in range(T_p):
+            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Y[t * (T // T_p):], T, d, BF, BF)
+    rs_ev[1].record()
+    torch.cuda.synchronize()
+    rs_us = 1e3 * rs_ev[0].elapsed_time(rs_ev[1]) / rs_reps
+    out["sequence_parallel"] = {
+        "what": "reduce-scatter of the 70B y(t) partials: each of 8 ranks sums its 2048 token rows",
+        "all_ranks_us": round(rs_us, 1), "per_rank_us": round(rs_us / T_p, 1),
+        "gbs": round(psum_bytes / (rs_us * 1e-6) / 1e9, 1),
+        "full_partial_sum_us": round(avg_us["psum"], 1)}
+    log(f"[bench] reduce-scatter: 8 ranks {rs_us:.1f} us (full sum {avg_us['psum']:.1f} us)")
+
     if not args.no_backward:
         out["backward"] = measure_backward(w, X, W1, W3, W2, max(2, args.steps // 4), 1)
     if not args.no_block:

@@ -275,6 +275,27 @@ int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p,
                    const void* residual, void* y, int64_t n_elems,
                    int32_t part_dtype, int32_t out_dtype, void* hip_stream);
 
+/*
+ * Sequence-parallel form of the sum ("7.9 Tensor and pipeline parallelism",
+ * section 2.5; "Parallelism II: model", "Sequence and context parallelism"):
+ * the all-reduce after the row shard becomes a reduce-scatter in which rank t
+ * keeps token rows [t*T/T_p, (t+1)*T/T_p) of y = sum_s y(s) (+ residual).
+ *
+ *   partials       T_p slices [T, d] at partial_stride elements (>= T*d), part_dtype
+ *   t              the rank whose rows are produced
+ *   residual       [T/T_p, d] out_dtype: rank t's rows of the residual stream (sharded
+ *                  by rows as well), or NULL; may equal y_rows
+ *   y_rows         [T/T_p, d] out_dtype: rank t's rows of the sum
+ * T_p must divide T (TP_ERR_NOT_DIVISIBLE) and d must be a multiple of 8.
+ * The values equal rows [t*T/T_p, ...) of tp_partial_sum over the same inputs bit
+ * for bit (same kernel, same ascending order).  The all-gather that follows, every
+ * rank's rows into the [T, d] input of the next column GEMM, is a placement on one
+ * GPU: pass y_rows = y + t*(T/T_p)*d.  Errors: as tp_partial_sum, plus the above.
+ */
+int tp_reduce_scatter_rows(const void* partials, int64_t partial_stride, int32_t T_p, int32_t t,
+                           const void* residual, void* y_rows, int64_t T, int64_t d,
+                           int32_t part_dtype, int32_t out_dtype, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -589,4 +589,26 @@ int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, co
                     "partial-sum launch");
 }
 
+int tp_reduce_scatter_rows(const void* partials, int64_t partial_stride, int32_t T_p, int32_t t,
+                           const void* residual, void* y_rows, int64_t T, int64_t d,
+                           int32_t part_dtype, int32_t out_dtype, void* hip_stream) {
+  const char* fn = "tp_reduce_scatter_rows";
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
+  if (T < 0 || T >= kMaxRows || d <= 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: T=%lld, d=%lld out of range", fn, (long long)T, (long long)d);
+  if (T % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "%s: T=%lld tokens not divisible by T_p=%d", fn, (long long)T, T_p);
+  if (d % 8) return fail(TP_ERR_UNSUPPORTED, "%s: d=%lld must be a multiple of 8", fn, (long long)d);
+  if (partial_stride < T * d)
+    return fail(TP_ERR_INVALID_ARG, "%s: partial_stride %lld < T*d", fn, (long long)partial_stride);
+  const int64_t rows = T / T_p;
+  const size_t pe = part_dtype == TP_BF16 ? 2 : 4;
+  TRY(check_ptr(partials, "partials"));
+  const void* first = (const char*)partials + (size_t)t * rows * d * pe;
+  // rank t's rows of every slice: the same kernel and order as the full sum, on a sub-range
+  return tp_partial_sum(first, partial_stride, T_p, residual, y_rows, rows * d, part_dtype, out_dtype,
+                        hip_stream);
+}
+
 }  // extern "C"

@@ -217,6 +217,24 @@ def partial_sum(parts, residual=None) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- attention
+def reduce_scatter_rows(parts, T_p: int, t: int, residual_rows=None) -> np.ndarray:
+    """Rank t's token rows of the sum, the sequence-parallel reduce-scatter.
+
+    "7.9 Tensor and pipeline parallelism" section 2.5 and "Parallelism II:
+    model", "Sequence and context parallelism": the all-reduce after the row
+    shard becomes a reduce-scatter over the sequence, rank t keeping rows
+    [t*T/T_p, (t+1)*T/T_p) (T_p must divide T), with its rows of the residual
+    stream added; an all-gather restores the full rows for the next column shard.
+    """
+    parts = [np.asarray(p_, dtype=np.float64) for p_ in parts]
+    T = parts[0].shape[0]
+    b, m = shard_range(T, T_p, t)
+    acc = np.zeros_like(parts[0][b:b + m])
+    for p_ in parts:
+        acc = acc + p_[b:b + m]
+    return acc if residual_rows is None else acc + np.asarray(residual_rows, dtype=np.float64)
+
+
 def attn_outproj_shard(o_t, wo, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
                        t: int) -> np.ndarray:
     """a(t) = O(t) . Wo[rows(t), :] -- row-sharded output projection.

@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 2
@@ -190,4 +190,21 @@ def test_backward_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_ffn_shard_bwd(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=1000, T_p=3), S.TP_ERR_NOT_DIVISIBLE),               # sequence not divisible by T_p
+    (dict(t=4), S.TP_ERR_INVALID_ARG),
+    (dict(d=100), S.TP_ERR_UNSUPPORTED),
+    (dict(partial_stride=100), S.TP_ERR_INVALID_ARG),
+    (dict(partials=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(part_dtype=5), S.TP_ERR_UNSUPPORTED),
+])
+def test_reduce_scatter_rejects_before_launch(kw, code):
+    a = dict(partials=P, partial_stride=1024 * 64, T_p=4, t=1, residual=None, y_rows=P + (1 << 24),
+             T=1024, d=64, part_dtype=S.TP_BF16, out_dtype=S.TP_BF16, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_reduce_scatter_rows(**a)
     assert e.value.code == code, S.tp_last_error()

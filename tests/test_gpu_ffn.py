@@ -203,6 +203,36 @@ def test_partial_sum_integers_exact_and_in_place():
     assert np.array_equal(host64(y), ref)
 
 
+@pytest.mark.parametrize("T_p,pd,od", [(8, S.TP_BF16, S.TP_BF16), (4, S.TP_F32, S.TP_BF16),
+                                        (2, S.TP_BF16, S.TP_F32)])
+def test_reduce_scatter_rows_are_the_sum_rows(T_p, pd, od):
+    """Sequence-parallel reduce-scatter: each rank's rows equal the same rows of the full
+    partial sum bit for bit, the oracle within rounding, and the ranks' rows gathered in
+    place form the full sum."""
+    T, d = 1032, 520
+    stride = T * d + 2048
+    g = np.random.default_rng(T_p + 10 * pd + 100 * od)
+    pdt = torch.bfloat16 if pd == S.TP_BF16 else torch.float32
+    odt = torch.bfloat16 if od == S.TP_BF16 else torch.float32
+    P = torch.from_numpy(g.standard_normal((T_p, stride)).astype(np.float32)).to(pdt).cuda()
+    res = torch.from_numpy(g.standard_normal((T, d)).astype(np.float32)).to(odt).cuda()
+    full = torch.empty((T, d), dtype=odt, device="cuda:0")
+    S.tp_partial_sum(P, stride, T_p, res, full, T * d, pd, od)
+    gathered = torch.full((T, d), float("nan"), dtype=odt, device="cuda:0")
+    m = T // T_p
+    for t in range(T_p):
+        S.tp_reduce_scatter_rows(P, stride, T_p, t, res[t * m:(t + 1) * m], gathered[t * m:(t + 1) * m],
+                                 T, d, pd, od)
+    torch.cuda.synchronize()
+    assert torch.equal(gathered, full)
+    Ph = host64(P)[:, :T * d].reshape(T_p, T, d)
+    rh = host64(res)
+    tol = 2 ** -8 if od == S.TP_BF16 else 4e-6
+    for t in (0, T_p - 1):
+        ref = O.reduce_scatter_rows(list(Ph), T_p, t, rh[t * m:(t + 1) * m])
+        assert nerr(host64(gathered[t * m:(t + 1) * m]), ref) <= tol
+
+
 def test_empty_inputs_are_noops():
     x = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda:0")
     w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda:0")

@@ -272,3 +272,20 @@ def test_bubble_four_stages_eight_micro_batches():
     assert analytic.bubble_fraction(4, 8) == Fraction(3, 11)
     # the two normalisations describe the same idle time
     assert analytic.bubble_vs_useful(4, 8) * 8 == analytic.bubble_fraction(4, 8) * 11
+
+
+@pytest.mark.parametrize("T_p", [1, 2, 4, 8])
+def test_reduce_scatter_rows_gather_to_the_all_reduce(T_p):
+    """The ranks' reduce-scatter rows, gathered in rank order, are the all-reduce's sum
+    (the same bytes split in two steps, "Parallelism II: model"); T_p must divide T."""
+    r = np.random.default_rng(17)
+    T, d = 24, 5
+    parts = [r.standard_normal((T, d)) for _ in range(T_p)]
+    res = r.standard_normal((T, d))
+    full = O.partial_sum(parts, res)
+    m = T // T_p
+    got = np.concatenate([O.reduce_scatter_rows(parts, T_p, t, res[t * m:(t + 1) * m]) for t in range(T_p)])
+    assert np.max(np.abs(got - full)) <= 1e-13
+    if T_p > 1:
+        with pytest.raises(ValueError):
+            O.reduce_scatter_rows([p[:T - 1] for p in parts], T_p, 0)
