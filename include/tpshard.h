@@ -158,6 +158,26 @@ int tp_ffn_shard_fwd_train(const void* x, const void* w1, const void* w3, const 
                            int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
                            int32_t act, int32_t out_dtype, void* hip_stream);
 
+/*
+ * Backward of rank t's out-projection a(t) = O(t) . Wo[rows(t), :]
+ * ("7.9 Tensor and pipeline parallelism", section 2.2, with the f-g pattern of
+ * section 2.1: the sum over ranks passes dY unchanged to every rank).
+ *
+ *   o_t   [T, h_t*head_dim] bf16: rank t's head outputs (the forward's input)
+ *   wo    [n_heads*head_dim, d] bf16, full matrix
+ *   dy    [T, d] bf16: dL/da for the summed output
+ *   do_t  [T, h_t*head_dim] bf16: dO(t) = dY Wo(t)^T, the gradient of rank t's heads
+ *         (no sum over ranks: each rank's heads are its own)
+ *   dwo   [n_heads*head_dim, d] grad_dtype (BF16/F32): rows of rank t's heads
+ *         := O(t)^T dY (overwritten; other rows untouched; zero when T = 0)
+ * Divisibility and shape rules as tp_attn_outproj_shard_fwd.  Two kernels.
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_NOT_DIVISIBLE, TP_ERR_UNSUPPORTED, TP_ERR_HIP.
+ */
+int tp_attn_outproj_shard_bwd(const void* o_t, const void* wo, const void* dy, void* do_t,
+                              void* dwo, int64_t T, int64_t d, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim, int32_t T_p, int32_t t,
+                              int32_t grad_dtype, void* hip_stream);
+
 /* Workspace of tp_ffn_shard_bwd: dU (and dV for the gated kinds), bf16 [T, n]
  * each, every plane rounded up to 256 bytes.  0 for invalid arguments. */
 size_t tp_ffn_bwd_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t act);

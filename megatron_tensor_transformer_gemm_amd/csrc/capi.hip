@@ -589,6 +589,67 @@ int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, co
                     "partial-sum launch");
 }
 
+int tp_attn_outproj_shard_bwd(const void* o_t, const void* wo, const void* dy, void* do_t, void* dwo,
+                              int64_t T, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t T_p, int32_t t, int32_t grad_dtype,
+                              void* hip_stream) {
+  const char* fn = "tp_attn_outproj_shard_bwd";
+  if (T < 0 || T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: T out of range", fn);
+  if (d <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: d, head counts and head_dim must be positive", fn);
+  if (T_p < 1 || t < 0 || t >= T_p)
+    return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
+  if (n_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+  if (n_kv_heads % T_p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+  if (n_heads % n_kv_heads)
+    return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
+  if (grad_dtype != TP_BF16 && grad_dtype != TP_F32)
+    return fail(TP_ERR_UNSUPPORTED, "%s: grad_dtype %d not supported", fn, grad_dtype);
+  const int64_t kdim = (int64_t)(n_heads / T_p) * head_dim;
+  if (d % 8 || kdim % 8 || d > kMaxExtent || (int64_t)n_heads * head_dim > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "%s: d and h_t*head_dim must be multiples of 8 (and at most %lld)",
+                fn, (long long)kMaxExtent);
+  TRY(check_ptr(o_t, "o_t"));
+  TRY(check_ptr(wo, "wo"));
+  TRY(check_ptr(dy, "dy"));
+  TRY(check_ptr(do_t, "do_t"));
+  TRY(check_ptr(dwo, "dwo"));
+  hipStream_t s = (hipStream_t)hip_stream;
+  const size_t r0 = (size_t)t * kdim;   // first row of rank t's block of Wo
+  if (T > 0) {
+    // dO(t) = dY Wo(t)^T: Wo's row block [kdim, d] is B^T
+    tpk::GemmDesc g{};
+    g.A = dy;
+    g.B0 = (const __bf16*)wo + r0 * (size_t)d;
+    g.C = do_t;
+    g.M = T;
+    g.N = (int32_t)kdim;
+    g.K = (int32_t)d;
+    g.lda = (int32_t)d;
+    g.ldb = (int32_t)d;
+    g.ldc = (int32_t)kdim;
+    g.act = TP_ACT_NONE;
+    g.out_f32 = false;
+    TRY(hip_status(tpk::launch_gemm_bf16_nt(g, s), "dO GEMM launch"));
+  }
+  // dWo[rows(t), :] = O(t)^T dY: O(t) [T, kdim] is A^T (k = 0 when T = 0: the block is zeroed)
+  tpk::GemmDesc g{};
+  g.A = o_t;
+  g.B0 = dy;
+  g.C = (char*)dwo + r0 * (size_t)d * (grad_dtype == TP_F32 ? 4 : 2);
+  g.M = kdim;
+  g.N = (int32_t)d;
+  g.K = (int32_t)T;
+  g.lda = (int32_t)kdim;
+  g.ldb = (int32_t)d;
+  g.ldc = (int32_t)d;
+  g.act = TP_ACT_NONE;
+  g.out_f32 = grad_dtype == TP_F32;
+  return hip_status(tpk::launch_gemm_bf16_tn(g, s), "dWo GEMM launch");
+}
+
 int tp_reduce_scatter_rows(const void* partials, int64_t partial_stride, int32_t T_p, int32_t t,
                            const void* residual, void* y_rows, int64_t T, int64_t d,
                            int32_t part_dtype, int32_t out_dtype, void* hip_stream) {

@@ -54,6 +54,8 @@ _SIGS = {
     "tp_ffn_shard_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
                                       _i32, _i32, _i32, _vp]),
     "tp_ffn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "tp_attn_outproj_shard_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _vp]),
     "tp_reduce_scatter_rows": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i64, _i32, _i32, _vp]),
     "tp_ffn_shard_bwd": (_i32, [_vp] * 12 + [_vp, _sz, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                              _vp]),
@@ -214,6 +216,13 @@ def tp_ffn_shard_bwd(x, w1, w3, w2, dy, h_t, u_t, v_t, dx_t, dw1, dw3, dw2, work
         _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(dy), _ptr(h_t), _ptr(u_t), _ptr(v_t), _ptr(dx_t),
         _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(workspace), workspace_bytes, T, d, d_ff, T_p, t, act,
         dx_dtype, grad_dtype, _stream(hip_stream)))
+
+
+def tp_attn_outproj_shard_bwd(o_t, wo, dy, do_t, dwo, T, d, n_heads, n_kv_heads, head_dim, T_p, t,
+                              grad_dtype, hip_stream=None):
+    _check("tp_attn_outproj_shard_bwd", lib().tp_attn_outproj_shard_bwd(
+        _ptr(o_t), _ptr(wo), _ptr(dy), _ptr(do_t), _ptr(dwo), T, d, n_heads, n_kv_heads, head_dim, T_p,
+        t, grad_dtype, _stream(hip_stream)))
 
 
 def tp_reduce_scatter_rows(partials, partial_stride, T_p, t, residual, y_rows, T, d, part_dtype,

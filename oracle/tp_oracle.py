@@ -251,6 +251,23 @@ def attn_outproj_shard(o_t, wo, n_heads: int, n_kv_heads: int, head_dim: int, T_
     return o_t @ np.asarray(wo[b:e, :], dtype=np.float64)
 
 
+def attn_outproj_shard_bwd(o_t, wo, dy, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
+                           t: int) -> dict:
+    """Backward of the row-sharded out-projection a(t) = O(t) . Wo[rows(t), :].
+
+    The same f-g pattern as the FFN ("7.9 ..." section 2.2 with 2.1): the sum
+    over ranks (g) passes dY unchanged to every rank; O(t) holds only rank t's
+    heads, so its gradient dO(t) = dY Wo(t)^T stays on the rank, and dWo(t) =
+    O(t)^T dY is rank t's block of rows of dWo.
+    """
+    hs = head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
+    b, e = hs["o_rows"]
+    o_t = np.asarray(o_t, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    wr = np.asarray(wo[b:e, :], dtype=np.float64)
+    return {"do_t": dy @ wr.T, "dwo": o_t.T @ dy}
+
+
 def attention_head(q, k, v, causal: bool = True, rows=None) -> np.ndarray:
     """softmax(Q K^T / sqrt(d_h) [+ causal mask]) V for one head.
 

@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 2
@@ -207,4 +207,21 @@ def test_reduce_scatter_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_reduce_scatter_rows(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_kv_heads=8, T_p=16), S.TP_ERR_NOT_DIVISIBLE),
+    (dict(t=8), S.TP_ERR_INVALID_ARG),
+    (dict(dy=None), S.TP_ERR_INVALID_ARG),
+    (dict(dwo=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(grad_dtype=4), S.TP_ERR_UNSUPPORTED),
+    (dict(d=8196), S.TP_ERR_UNSUPPORTED),
+])
+def test_outproj_backward_rejects_before_launch(kw, code):
+    a = dict(o_t=P, wo=P, dy=P, do_t=P, dwo=P, T=16, d=8192, n_heads=64, n_kv_heads=8, head_dim=128,
+             T_p=8, t=0, grad_dtype=S.TP_F32, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_outproj_shard_bwd(**a)
     assert e.value.code == code, S.tp_last_error()

@@ -252,3 +252,74 @@ def test_backward_llama3_8b_shape_sampled():
 @pytest.mark.slow
 def test_backward_llama3_70b_shape_sampled():
     _sampled_backward(I.WORKLOADS[4], t=3, n_rows=128, n_cols=8)
+
+
+# ----------------------------------------------------------------------------- out-projection backward
+def _outproj_bwd(od, wod, dyd, T, d, H, KV, dh, T_p, t, gc):
+    k = H // T_p * dh
+    do = torch.full((T, k), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    dwo = torch.full((H * dh, d), SENTINEL, dtype=_tdt(gc), device="cuda:0")
+    S.tp_attn_outproj_shard_bwd(od, wod, dyd, do, dwo, T, d, H, KV, dh, T_p, t, gc)
+    torch.cuda.synchronize()
+    return do, dwo
+
+
+def test_outproj_backward_integer_bit_exact():
+    """O(t) integers in [-8, 8], Wo with one +-1 per row, dY integers in [-4, 4]: dO(t) (bf16)
+    and the fp32 dWo block are exact integers, equal to the oracle bit for bit."""
+    T, d, H, KV, dh, T_p = 1000, 520, 16, 8, 64, 4
+    k = H // T_p * dh
+    g = np.random.default_rng(31)
+    o = g.integers(-8, 9, (T, H * dh)).astype(np.float32)
+    wo = np.zeros((H * dh, d), dtype=np.float32)
+    rows = np.arange(H * dh)
+    wo[rows, (5 * rows + 2) % d] = g.choice([-1.0, 1.0], H * dh)
+    dy = g.integers(-4, 5, (T, d)).astype(np.float32)
+    wod, dyd = dev(I.bf16_bits(wo), I.BF16), dev(I.bf16_bits(dy), I.BF16)
+    for t in range(T_p):
+        od = dev(I.bf16_bits(np.ascontiguousarray(o[:, t * k:(t + 1) * k])), I.BF16)
+        do, dwo = _outproj_bwd(od, wod, dyd, T, d, H, KV, dh, T_p, t, S.TP_F32)
+        ref = O.attn_outproj_shard_bwd(o[:, t * k:(t + 1) * k], wo, dy, H, KV, dh, T_p, t)
+        assert np.array_equal(host64(do), ref["do_t"]), f"dO({t}) differs"
+        gw = host64(dwo)
+        assert np.array_equal(gw[t * k:(t + 1) * k], ref["dwo"]), f"dWo block {t} differs"
+        _check_untouched(gw, t * k, (t + 1) * k, 0, "dWo")
+
+
+@pytest.mark.parametrize("gc", [S.TP_F32, S.TP_BF16])
+def test_outproj_backward_parity(gc):
+    T, d, H, KV, dh, T_p, t = 777, 392, 12, 6, 128, 3, 2
+    k = H // T_p * dh
+    g = np.random.default_rng(41 + gc)
+    o = I.bf16_bits(g.standard_normal((T, k)).astype(np.float32))
+    wo = I.bf16_bits((g.standard_normal((H * dh, d)) / np.sqrt(H * dh)).astype(np.float32))
+    dy = I.bf16_bits(g.standard_normal((T, d)).astype(np.float32))
+    do, dwo = _outproj_bwd(dev(o, I.BF16), dev(wo, I.BF16), dev(dy, I.BF16), T, d, H, KV, dh, T_p, t, gc)
+    ref = O.attn_outproj_shard_bwd(f64(o, I.BF16), f64(wo, I.BF16), f64(dy, I.BF16), H, KV, dh, T_p, t)
+    e1 = nerr(host64(do), ref["do_t"])
+    e2 = nerr(host64(dwo)[t * k:(t + 1) * k], ref["dwo"])
+    log(f"[outproj-bwd] grad dtype {gc}: dO {e1:.2e} dWo {e2:.2e}")
+    assert e1 < BF16_TOL and e2 < BF16_TOL
+    _check_untouched(host64(dwo), t * k, (t + 1) * k, 0, "dWo")
+
+
+@pytest.mark.slow
+def test_outproj_backward_llama3_70b_shape_sampled():
+    w = I.WORKLOADS[4]
+    T, d, H, KV, dh, T_p, t = w.T, w.d, w.n_heads, w.n_kv_heads, w.head_dim, w.T_p, 6
+    k = H // T_p * dh
+    log(f"[outproj-bwd-full] {w.name} t={t}")
+    o_full = I.make_tensor(w, "o")
+    o = np.ascontiguousarray(o_full[:, t * k:(t + 1) * k])
+    wo = I.make_tensor(w, "wo")
+    dy = I.make_tensor(w, "dy")
+    do, dwo = _outproj_bwd(dev(o, w.dtype), dev(wo, w.dtype), dev(dy, w.dtype), T, d, H, KV, dh, T_p, t,
+                           S.TP_F32)
+    dy64 = f64(dy, w.dtype)
+    wr = f64(wo[t * k:(t + 1) * k], w.dtype)
+    rows = sample_rows(T, 256, 77)
+    e1 = nerr(host64(do[torch.as_tensor(rows, device="cuda:0")]), dy64[rows] @ wr.T)
+    cols = np.unique(np.concatenate([[0, k - 1], np.random.default_rng(5).choice(k, 16, False)]))
+    e2 = nerr(host64(dwo)[t * k + cols], f64(o[:, cols], w.dtype).T @ dy64)
+    log(f"[outproj-bwd-full] dO {e1:.2e} dWo {e2:.2e}")
+    assert e1 < BF16_TOL and e2 < BF16_TOL

@@ -1,4 +1,4 @@
-"""Pins of the oracle's FFN backward (CPU only).
+"""Pins of the oracle's backward of the row-sharded products (FFN, out-projection; CPU only).
 
 The pages give the f-g pattern ("7.9 Tensor and pipeline parallelism", section
 2.1): the rank's input gradient is a partial sum that f all-reduces, the
@@ -139,3 +139,29 @@ def test_backward_single_rank_input_gradient_is_partial():
     full = O.ffn_shard_bwd(x, w1, w3, w2, dy, 1, 0, "gelu")["dx_t"]
     part = O.ffn_shard_bwd(x, w1, w3, w2, dy, 4, 1, "gelu")["dx_t"]
     assert np.max(np.abs(part - full)) > 1e-3 * np.max(np.abs(full))
+
+
+def test_outproj_backward_matches_autograd_and_assembles():
+    """dO(t) and dWo(t) against float64 autograd of a = O Wo, and the ranks' pieces against the
+    unsharded gradients: dO(t) is rank t's head columns of dO, dWo(t) its head rows of dWo."""
+    r = np.random.default_rng(21)
+    T, d, H, dh, T_p = 7, 12, 8, 4, 4
+    o = r.standard_normal((T, H * dh))
+    wo = r.standard_normal((H * dh, d))
+    dy = r.standard_normal((T, d))
+    to = torch.tensor(o, requires_grad=True)
+    tw = torch.tensor(wo, requires_grad=True)
+    ((to @ tw) * torch.tensor(dy)).sum().backward()
+    k = H * dh // T_p
+    for t in range(T_p):
+        g = O.attn_outproj_shard_bwd(o[:, t * k:(t + 1) * k], wo, dy, H, H // 2, dh, T_p, t)
+        assert np.max(np.abs(g["do_t"] - to.grad.numpy()[:, t * k:(t + 1) * k])) < 1e-12
+        assert np.max(np.abs(g["dwo"] - tw.grad.numpy()[t * k:(t + 1) * k])) < 1e-12
+    # finite differences on one entry of Wo and one of O(t)
+    eps = 1e-6
+    g = O.attn_outproj_shard_bwd(o[:, k:2 * k], wo, dy, H, H // 2, dh, T_p, 1)
+    wp, wm = wo.copy(), wo.copy()
+    wp[k + 3, 5] += eps
+    wm[k + 3, 5] -= eps
+    fd = (np.sum((o @ wp) * dy) - np.sum((o @ wm) * dy)) / (2 * eps)
+    assert abs(fd - g["dwo"][3, 5]) < 1e-7 * max(1.0, abs(fd))
