@@ -494,7 +494,10 @@ hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
 
 // Tile choice: 256x256 tiles once they give at least one full wave of workgroups over the
 // 256 CUs, else 128x128 (or 128x256 for the gated pair).  Long k-loops use 4 stages of 32 k
-// (more copies in flight); short ones 2 stages of 64 k (fewer, longer stages).
+// (more copies in flight); short ones 2 stages of 64 k (fewer, longer stages).  With both
+// operands k-contiguous (kNT) every tile row is a k-run in memory, and 64-k stages fetch
+// whole 128-byte lines: measured 2-5% faster than 32-k stages at every depth; there a last
+// wave of 256x256 tiles at most 3/4 full switches to 128x256 tiles.
 template <bool DUAL, int ACT, bool OUT_F32, int LAYOUT = kNN, bool SAVE = false>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
@@ -502,6 +505,13 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) ncols += g.Nx[i];
   const int64_t big = ((g.M + 255) / 256) * ((ncols + OUT_BN - 1) / OUT_BN);
   const int64_t kdepth = (int64_t)g.K + (LAYOUT == kNT ? g.K2 : 0);
+  if constexpr (LAYOUT == kNT) {
+    if (big >= 256) {
+      const int64_t last = big % 256;
+      if (last != 0 && last <= 192) return launch_cfg<128, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+    }
+  }
   if (big >= 256) {
     if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
     return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);

@@ -190,7 +190,8 @@ def test_attention_gqa_divisibility_rejected():
 
 
 @pytest.mark.parametrize("L,h_t,kv_t,dh,causal", [(300, 4, 2, 128, True), (96, 2, 2, 64, False),
-                                                  (700, 2, 1, 64, True), (2048, 6, 6, 128, True)])
+                                                  (700, 2, 1, 64, True), (2048, 6, 6, 128, True),
+                                                  (1000, 3, 3, 64, True), (129, 1, 1, 128, True)])
 def test_attention_core_parity_strided(L, h_t, kv_t, dh, causal):
     """tp_attn_core_fwd on projected heads stored with padded leading dimensions."""
     n_seq = 2 if L < 2048 else 1
