@@ -73,7 +73,7 @@ struct Flag {
 constexpr float kLazy = 8.0f;  // log2 of the largest exponential kept before rescaling
 
 template <int DH>
-__global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int nqb) {
+__global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int nqb, int strands) {
   constexpr int CPR = DH / 8;           // 16-byte chunks per row
   constexpr int ROWB = DH * 2;          // bytes per row
   constexpr int TILE = kBK * ROWB;      // one K or V block
@@ -95,8 +95,23 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
   const int g = wave >> 1;    // key group
   const int qh = wave & 1;    // which 32 of the 64 queries
   const int S = a.seq_len;
-  const int qb = nqb - 1 - (int)(blockIdx.x / (unsigned)a.h_t);  // latest (heaviest) first
-  const int j = (int)(blockIdx.x % (unsigned)a.h_t);              // local query head
+  // Workgroups are dealt round-robin over the 8 XCDs.  With `strands` = G > 0 each head's
+  // query blocks form G strands (qb mod G), heaviest first, h_t*G a multiple of 8: XCD x
+  // takes h_t*G/8 adjacent strands (the K/V of at most two heads through its L2), and its
+  // slot i runs level i / (strands per XCD), so every XCD proceeds heaviest first.
+  // Otherwise (G = 0): latest (heaviest) block positions first, all heads of a position
+  // together.
+  int j, qb;
+  if (strands > 0) {
+    const int spx = a.h_t * strands / 8;
+    const int x = (int)(blockIdx.x & 7u), i = (int)(blockIdx.x >> 3);
+    const int sidx = x * spx + i % spx;
+    j = sidx / strands;
+    qb = nqb - strands + sidx % strands - strands * (i / spx);
+  } else {
+    qb = nqb - 1 - (int)(blockIdx.x / (unsigned)a.h_t);
+    j = (int)(blockIdx.x % (unsigned)a.h_t);
+  }
   const int64_t seq = blockIdx.y;
   const int kvh = j / (a.h_t / a.kv_t);
   const int q0 = qb * kBQ;
@@ -389,10 +404,13 @@ hipError_t launch_attention(const AttnDesc& a, hipStream_t s) {
   const int64_t nqb = (a.seq_len + kBQ - 1) / kBQ;
   if (a.n_seq > 65535 || a.h_t <= 0 || nqb * a.h_t > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(nqb * a.h_t), (unsigned)a.n_seq);
+  int g8 = 8;
+  while (a.h_t % g8) g8 >>= 1;   // gcd(h_t, 8)
+  const int strands = nqb % (8 / g8) == 0 ? 8 / g8 : 0;
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb);
+    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
   else if (a.head_dim == 64)
-    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb);
+    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
