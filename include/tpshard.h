@@ -260,6 +260,30 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
                             int32_t T_p, int32_t t, int32_t causal, void* hip_stream);
 
 /*
+ * tp_attn_heads_shard_fwd for tensor-parallel degrees above the KV head count
+ * (grouped-query attention): "Tensor & Pipeline Parallelism" (S17), "Attention
+ * shards by head, and GQA caps the degree" -- TP16 with 8 KV heads needs KV heads
+ * replicated across ranks.  When T_p is a multiple of n_kv_heads, each KV head
+ * serves T_p / n_kv_heads consecutive ranks: rank t projects and uses KV head
+ * t / (T_p / n_kv_heads) for all of its h_t = n_heads / T_p query heads.  When T_p
+ * divides n_kv_heads this is exactly tp_attn_heads_shard_fwd.  Same arguments;
+ * workspace >= tp_attn_heads_kvrep_workspace_bytes(...).
+ * Errors: as tp_attn_heads_shard_fwd; TP_ERR_NOT_DIVISIBLE when neither T_p divides
+ * n_kv_heads nor n_kv_heads divides T_p.
+ */
+int tp_attn_heads_shard_fwd_kvrep(const void* x, const void* wq, const void* wk, const void* wv,
+                                  void* o_t, void* workspace, size_t workspace_bytes,
+                                  int64_t n_seq, int64_t seq_len, int64_t d,
+                                  int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t T_p, int32_t t, int32_t causal, void* hip_stream);
+
+/* Workspace of tp_attn_heads_shard_fwd_kvrep: Q of the h_t query heads, K and V of the
+ * rank's KV heads (one when replicated), n_seq*seq_len rows, bf16, rounded up to 256.
+ * 0 for invalid arguments. */
+size_t tp_attn_heads_kvrep_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t T_p);
+
+/*
  * The attention core alone (the second half of tp_attn_heads_shard_fwd), on the rank's
  * already-projected heads: for each local query head j and sequence s,
  *     O_j = softmax(Q_j K_kv(j)^T / sqrt(head_dim) [+ causal mask]) V_kv(j),

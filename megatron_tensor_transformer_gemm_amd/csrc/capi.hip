@@ -432,12 +432,27 @@ size_t tp_attn_heads_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_h
   return round256((size_t)(n_seq * seq_len) * (size_t)((h_t + 2 * kv_t) * head_dim) * 2);
 }
 
-int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const void* wv,
-                            void* o_t, void* workspace, size_t workspace_bytes, int64_t n_seq,
-                            int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
-                            int32_t head_dim, int32_t T_p, int32_t t, int32_t causal,
-                            void* hip_stream) {
-  const char* fn = "tp_attn_heads_shard_fwd";
+size_t tp_attn_heads_kvrep_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t T_p) {
+  if (n_seq < 0 || seq_len < 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || T_p < 1) return 0;
+  if (n_kv_heads % T_p == 0)
+    return tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
+  if (n_heads % T_p || T_p % n_kv_heads || n_heads % n_kv_heads) return 0;
+  // one (replicated) KV head per rank
+  return round256((size_t)(n_seq * seq_len) * (size_t)((n_heads / T_p + 2) * head_dim) * 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of tp_attn_heads_shard_fwd and tp_attn_heads_shard_fwd_kvrep.  With kvrep
+// and fewer KV heads than ranks, each KV head serves T_p / n_kv_heads consecutive ranks
+// and rank t reads KV head t / (T_p / n_kv_heads) for all of its query heads.
+int attn_heads_impl(const char* fn, bool kvrep, const void* x, const void* wq, const void* wk,
+                    const void* wv, void* o_t, void* workspace, size_t workspace_bytes,
+                    int64_t n_seq, int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t T_p, int32_t t, int32_t causal, void* hip_stream) {
   if (n_seq < 0 || seq_len < 0 || n_seq > 65535)
     return fail(TP_ERR_INVALID_ARG, "%s: n_seq=%lld / seq_len=%lld out of range", fn, (long long)n_seq,
                 (long long)seq_len);
@@ -447,7 +462,11 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
     return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
   if (n_heads % T_p)
     return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
-  if (n_kv_heads % T_p)
+  const bool replicate = kvrep && n_kv_heads % T_p != 0;
+  if (replicate && T_p % n_kv_heads)
+    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d cannot replicate %d KV heads evenly (T_p must be a multiple)",
+                T_p, n_kv_heads);
+  if (!replicate && n_kv_heads % T_p)
     return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
   if (n_heads % n_kv_heads)
     return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
@@ -459,7 +478,9 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
     return fail(TP_ERR_UNSUPPORTED, "%s: extent too large", fn);
   const int64_t T = n_seq * seq_len;
   if (T >= kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: too many tokens", fn);
-  const int64_t h_t = n_heads / T_p, kv_t = n_kv_heads / T_p;
+  const int64_t h_t = n_heads / T_p, kv_t = replicate ? 1 : n_kv_heads / T_p;
+  // first KV head of rank t
+  const int64_t kv0 = replicate ? t / (T_p / n_kv_heads) : (int64_t)t * kv_t;
   // the attention kernel addresses one sequence of a head with 32-bit byte offsets
   if ((int64_t)seq_len * (h_t + 2 * kv_t) * head_dim * 2 >= (int64_t(1) << 30))
     return fail(TP_ERR_UNSUPPORTED, "%s: seq_len too long for one call", fn);
@@ -468,7 +489,8 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
   TRY(check_ptr(wk, "wk"));
   TRY(check_ptr(wv, "wv"));
   TRY(check_ptr(o_t, "o_t"));
-  const size_t need = tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
+  const size_t need = kvrep ? tp_attn_heads_kvrep_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p)
+                            : tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
   if (T > 0) {
     if (!workspace) return fail(TP_ERR_WORKSPACE, "%s: workspace is NULL", fn);
     if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -499,7 +521,7 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
   const void* wkv[2] = {wk, wv};
   __bf16* outs[2] = {k, v};
   for (int i = 0; i < 2; ++i) {
-    g.Bx[i] = (const __bf16*)wkv[i] + (size_t)t * kv_t * head_dim;
+    g.Bx[i] = (const __bf16*)wkv[i] + (size_t)kv0 * head_dim;
     g.Cx[i] = outs[i];
     g.Nx[i] = (int32_t)(kv_t * head_dim);
     g.ldbx[i] = (int32_t)(n_kv_heads * head_dim);
@@ -521,6 +543,30 @@ int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const
   a.ldo = (int32_t)(h_t * head_dim);
   a.causal = causal != 0;
   return hip_status(tpk::launch_attention(a, s), "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_attn_heads_shard_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                            void* o_t, void* workspace, size_t workspace_bytes, int64_t n_seq,
+                            int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t T_p, int32_t t, int32_t causal,
+                            void* hip_stream) {
+  return attn_heads_impl("tp_attn_heads_shard_fwd", false, x, wq, wk, wv, o_t, workspace,
+                         workspace_bytes, n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t,
+                         causal, hip_stream);
+}
+
+int tp_attn_heads_shard_fwd_kvrep(const void* x, const void* wq, const void* wk, const void* wv,
+                                  void* o_t, void* workspace, size_t workspace_bytes, int64_t n_seq,
+                                  int64_t seq_len, int64_t d, int32_t n_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t T_p, int32_t t, int32_t causal,
+                                  void* hip_stream) {
+  return attn_heads_impl("tp_attn_heads_shard_fwd_kvrep", true, x, wq, wk, wv, o_t, workspace,
+                         workspace_bytes, n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t,
+                         causal, hip_stream);
 }
 
 int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64_t n_seq,

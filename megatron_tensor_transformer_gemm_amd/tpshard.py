@@ -48,6 +48,9 @@ _SIGS = {
     "tp_attn_heads_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "tp_attn_heads_shard_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _vp]),
+    "tp_attn_heads_shard_fwd_kvrep": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32,
+                                             _i32, _i32, _i32, _i32, _i32, _vp]),
+    "tp_attn_heads_kvrep_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "tp_attn_core_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                 _i32, _vp]),
     "tp_partial_sum": (_i32, [_vp, _i64, _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
@@ -174,6 +177,18 @@ def tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim,
 def tp_attn_heads_shard_fwd(x, wq, wk, wv, o_t, workspace, workspace_bytes, n_seq, seq_len, d,
                             n_heads, n_kv_heads, head_dim, T_p, t, causal, hip_stream=None):
     _check("tp_attn_heads_shard_fwd", lib().tp_attn_heads_shard_fwd(
+        _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(o_t), _ptr(workspace), workspace_bytes,
+        n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t, int(causal),
+        _stream(hip_stream)))
+
+
+def tp_attn_heads_kvrep_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p) -> int:
+    return lib().tp_attn_heads_kvrep_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p)
+
+
+def tp_attn_heads_shard_fwd_kvrep(x, wq, wk, wv, o_t, workspace, workspace_bytes, n_seq, seq_len, d,
+                                  n_heads, n_kv_heads, head_dim, T_p, t, causal, hip_stream=None):
+    _check("tp_attn_heads_shard_fwd_kvrep", lib().tp_attn_heads_shard_fwd_kvrep(
         _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(o_t), _ptr(workspace), workspace_bytes,
         n_seq, seq_len, d, n_heads, n_kv_heads, head_dim, T_p, t, int(causal),
         _stream(hip_stream)))

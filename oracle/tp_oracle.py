@@ -62,6 +62,35 @@ def head_shard(n_heads: int, n_kv_heads: int, head_dim: int, T_p: int, t: int) -
     }
 
 
+def head_shard_kv_replicated(n_heads: int, n_kv_heads: int, head_dim: int, T_p: int, t: int) -> dict:
+    """Head shard of rank t when T_p exceeds the KV heads: the KV heads are replicated.
+
+    "Tensor & Pipeline Parallelism" (S17), "Attention shards by head, and GQA
+    caps the degree": with fewer KV heads than ranks the degree only works if
+    KV heads are replicated across ranks.  With T_p a multiple of n_kv_heads,
+    each KV head serves T_p / n_kv_heads consecutive ranks, and all h_t query
+    heads of rank t share KV head t // (T_p / n_kv_heads).  When T_p divides
+    n_kv_heads nothing is replicated and this is head_shard.
+    """
+    if n_kv_heads % T_p == 0:
+        return head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
+    if n_heads % T_p:
+        raise ValueError(f"TP degree {T_p} must divide query heads ({n_heads})")
+    if T_p % n_kv_heads or n_heads % n_kv_heads:
+        raise ValueError(f"TP{T_p} cannot replicate {n_kv_heads} KV heads evenly")
+    if not (0 <= t < T_p):
+        raise ValueError(f"rank {t} out of range for T_p={T_p}")
+    h_t = n_heads // T_p
+    kv = t // (T_p // n_kv_heads)
+    return {
+        "h_t": h_t,
+        "kv_t": 1,
+        "q_cols": (t * h_t * head_dim, (t + 1) * h_t * head_dim),
+        "kv_cols": (kv * head_dim, (kv + 1) * head_dim),
+        "o_rows": (t * h_t * head_dim, (t + 1) * h_t * head_dim),
+    }
+
+
 # ----------------------------------------------------------------------------- activations
 def gelu(u: np.ndarray) -> np.ndarray:
     """GELU, erf form: u * Phi(u) = u/2 * (1 + erf(u / sqrt 2)) = u/2 * erfc(-u / sqrt 2).
@@ -293,16 +322,16 @@ def attention_head(q, k, v, causal: bool = True, rows=None) -> np.ndarray:
 
 
 def attn_heads_shard(x, wq, wk, wv, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
-                     t: int, causal: bool = True, rows=None) -> np.ndarray:
+                     t: int, causal: bool = True, rows=None, kv_replicate: bool = False) -> np.ndarray:
     """O(t): the rank's heads' outputs concatenated, [T (or len(rows)), h_t*head_dim].
 
     Column shards of Wq (and of Wk/Wv by KV head) by head, per S17
     "Implementation" (``w.wq[:, h]``, KV sharded by KV head); local query head
     j of rank t reads KV head j // (h_t / kv_t) of that rank (grouped-query
     attention; with n_kv_heads == n_heads this is ordinary multi-head
-    attention).
+    attention).  kv_replicate takes head_shard_kv_replicated's blocks.
     """
-    hs = head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
+    hs = (head_shard_kv_replicated if kv_replicate else head_shard)(n_heads, n_kv_heads, head_dim, T_p, t)
     x = np.asarray(x, dtype=np.float64)
     qb, _ = hs["q_cols"]
     kb, _ = hs["kv_cols"]

@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 2
@@ -53,6 +53,11 @@ def test_workspace_queries():
     assert S.tp_ffn_workspace_bytes(64, 1024, 2, 7) == 0
     assert S.tp_attn_heads_workspace_bytes(1, 2048, 48, 48, 128, 8) == 2048 * 18 * 128 * 2
     assert S.tp_attn_heads_workspace_bytes(1, 2048, 64, 8, 128, 16) == 0
+    # TP16 over 8 KV heads: 4 query heads and one replicated KV head per rank
+    assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 64, 8, 128, 16) == 2048 * 6 * 128 * 2
+    assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 64, 8, 128, 8) == \
+        S.tp_attn_heads_workspace_bytes(1, 2048, 64, 8, 128, 8)
+    assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 48, 6, 128, 16) == 0
 
 
 def _ffn(**kw):
@@ -224,4 +229,19 @@ def test_outproj_backward_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_attn_outproj_shard_bwd(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_heads=48, n_kv_heads=6, T_p=16), S.TP_ERR_NOT_DIVISIBLE),   # 6 KV heads over 16 ranks
+    (dict(n_heads=60, T_p=16), S.TP_ERR_NOT_DIVISIBLE),                 # query heads not divisible
+    (dict(t=16), S.TP_ERR_INVALID_ARG),
+    (dict(workspace_bytes=1000), S.TP_ERR_WORKSPACE),
+])
+def test_kvrep_rejects_before_launch(kw, code):
+    a = dict(x=P, wq=P, wk=P, wv=P, o_t=P, workspace=P, workspace_bytes=1 << 30, n_seq=1, seq_len=256,
+             d=512, n_heads=64, n_kv_heads=8, head_dim=128, T_p=16, t=0, causal=True, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_heads_shard_fwd_kvrep(**a)
     assert e.value.code == code, S.tp_last_error()

@@ -215,3 +215,41 @@ def test_attention_core_parity_strided(L, h_t, kv_t, dh, causal):
                                    v64[r, kv * dh:(kv + 1) * dh], causal=causal)
             assert nerr(og[r, j * dh:(j + 1) * dh], ref) <= BF16_TOL, (s, j)
     assert np.all(og[:, h_t * dh:] == 5.0)          # padding columns untouched
+
+
+@pytest.mark.parametrize("n_heads,n_kv,T_p,dh", [(16, 2, 8, 64), (8, 1, 4, 128), (16, 4, 2, 128)])
+def test_attention_heads_kv_replicated_parity(n_heads, n_kv, T_p, dh):
+    """T_p above the KV heads: each KV head replicated on T_p / n_kv ranks; every rank against
+    the oracle's replicated reading.  When T_p divides n_kv the result equals the plain entry
+    point bit for bit."""
+    n_seq, L, d = 2, 200, 256
+    T = n_seq * L
+    log(f"[kvrep] H={n_heads} KV={n_kv} T_p={T_p} dh={dh}")
+    g = np.random.default_rng(n_heads * 100 + n_kv * 10 + T_p)
+    x = I.bf16_bits(g.standard_normal((T, d)).astype(np.float32))
+    wq = I.bf16_bits((g.standard_normal((d, n_heads * dh)) * 0.05).astype(np.float32))
+    wk = I.bf16_bits((g.standard_normal((d, n_kv * dh)) * 0.05).astype(np.float32))
+    wv = I.bf16_bits((g.standard_normal((d, n_kv * dh)) * 0.05).astype(np.float32))
+    xd, wqd, wkd, wvd = (dev(a, I.BF16) for a in (x, wq, wk, wv))
+    x64, wq64, wk64, wv64 = (f64(a, I.BF16) for a in (x, wq, wk, wv))
+    h_t = n_heads // T_p
+    nb = S.tp_attn_heads_kvrep_workspace_bytes(n_seq, L, n_heads, n_kv, dh, T_p)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    for t in range(T_p):
+        o = torch.full((T, h_t * dh), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        S.tp_attn_heads_shard_fwd_kvrep(xd, wqd, wkd, wvd, o, ws, nb, n_seq, L, d, n_heads, n_kv, dh,
+                                        T_p, t, True)
+        torch.cuda.synchronize()
+        og = host64(o)
+        ref = np.concatenate([O.attn_heads_shard(x64[s * L:(s + 1) * L], wq64, wk64, wv64, n_heads, n_kv,
+                                                 dh, T_p, t, causal=True, kv_replicate=True)
+                              for s in range(n_seq)])
+        assert nerr(og, ref) <= BF16_TOL, t
+        if n_kv % T_p == 0:
+            o2 = torch.empty_like(o)
+            ws2 = torch.empty(S.tp_attn_heads_workspace_bytes(n_seq, L, n_heads, n_kv, dh, T_p),
+                              dtype=torch.uint8, device="cuda:0")
+            S.tp_attn_heads_shard_fwd(xd, wqd, wkd, wvd, o2, ws2, ws2.numel(), n_seq, L, d, n_heads, n_kv,
+                                      dh, T_p, t, True)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o2)

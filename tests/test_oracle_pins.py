@@ -217,6 +217,42 @@ def test_block_sharded_equals_unsharded_and_rows():
     np.testing.assert_allclose(y_r, y[rows], atol=1e-12)
 
 
+@pytest.mark.parametrize("n_heads,n_kv,T_p", [(16, 2, 4), (16, 2, 8), (8, 1, 8), (16, 4, 2)])
+def test_kv_replicated_shards_equal_full_gqa(n_heads, n_kv, T_p):
+    """With T_p above the KV heads (each KV head replicated on T_p / n_kv ranks), the ranks'
+    O(t) concatenate to the unsharded grouped-query output written out by brute force; with
+    T_p dividing n_kv the replicated reading is the plain head shard."""
+    rng = np.random.default_rng(23)
+    T, d, dh = 6, 10, 4
+    x = rng.standard_normal((T, d))
+    wq = rng.standard_normal((d, n_heads * dh)) / math.sqrt(d)
+    wk = rng.standard_normal((d, n_kv * dh)) / math.sqrt(d)
+    wv = rng.standard_normal((d, n_kv * dh)) / math.sqrt(d)
+    g = n_heads // n_kv
+    heads = [np.array(_brute.attention((x @ wq[:, j * dh:(j + 1) * dh]).tolist(),
+                                       (x @ wk[:, (j // g) * dh:(j // g + 1) * dh]).tolist(),
+                                       (x @ wv[:, (j // g) * dh:(j // g + 1) * dh]).tolist()))
+             for j in range(n_heads)]
+    o_full = np.concatenate(heads, axis=1)
+    parts = [O.attn_heads_shard(x, wq, wk, wv, n_heads, n_kv, dh, T_p, t, kv_replicate=True)
+             for t in range(T_p)]
+    np.testing.assert_allclose(np.concatenate(parts, axis=1), o_full, atol=1e-13)
+    if n_kv % T_p == 0:
+        assert O.head_shard_kv_replicated(n_heads, n_kv, dh, T_p, 1) == O.head_shard(n_heads, n_kv, dh, T_p, 1)
+    else:
+        hs = O.head_shard_kv_replicated(n_heads, n_kv, dh, T_p, T_p - 1)
+        assert hs["kv_t"] == 1 and hs["kv_cols"] == ((n_kv - 1) * dh, n_kv * dh)
+
+
+def test_kv_replication_needs_an_even_multiple():
+    """Llama-3-70B-shaped 64 query / 8 KV heads: TP16 works by replicating each KV head on 2
+    ranks; 6 KV heads cannot be spread evenly over 16 ranks."""
+    hs = O.head_shard_kv_replicated(64, 8, 128, 16, 5)
+    assert hs["h_t"] == 4 and hs["kv_cols"] == (2 * 128, 3 * 128) and hs["q_cols"] == (5 * 512, 6 * 512)
+    with pytest.raises(ValueError, match="replicate"):
+        O.head_shard_kv_replicated(48, 6, 128, 16, 0)
+
+
 def test_gqa_divisibility():
     with pytest.raises(ValueError, match="n_kv_heads"):
         O.head_shard(64, 8, 128, 16, 0)
