@@ -512,6 +512,21 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
       return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
     }
   }
+  if constexpr (LAYOUT == kNN && !DUAL) {
+    // Forward products of a few thousand tokens (measured at 2048 x 2304..6144 x 768..6144):
+    // 256x256 tiles already pay off when they occupy 3/4 of the CUs, else 256x128 tiles
+    // when those occupy half of them; 128x128 only below that.
+    if (big >= 192) {
+      if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+    }
+    int64_t half = (g.N + 127) / 128;
+    for (int i = 0; i + 1 < g.nseg; ++i) half += (g.Nx[i] + 127) / 128;
+    if (((g.M + 255) / 256) * half >= 128) {
+      if (kdepth > 2048) return launch_cfg<256, 128, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      return launch_cfg<256, 128, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+    }
+  }
   if (big >= 256) {
     if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
     return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
