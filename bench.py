@@ -264,24 +264,30 @@ def main() -> int:
         "roofline": roofline,
     }
 
-    # sequence-parallel form of the same reduce: 8 ranks' row slices (reduce-scatter)
+    # sequence-parallel form of the same reduce: 8 ranks' row slices (reduce-scatter), into
+    # a buffer of its own (Y and A keep the step's results for the CPU comparison)
+    Yrs = torch.empty_like(Y)
     rs_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     rs_reps = 5
     for _ in range(2):
         for t in range(T_p):
-            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Y[t * (T // T_p):], T, d, BF, BF)
+            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Yrs[t * (T // T_p):], T, d, BF, BF)
     rs_ev[0].record()
     for _ in range(rs_reps):
         for t in range(T_p):
-            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Y[t * (T // T_p):], T, d, BF, BF)
+            S.tp_reduce_scatter_rows(P_flat, stride, T_p, t, None, Yrs[t * (T // T_p):], T, d, BF, BF)
     rs_ev[1].record()
     torch.cuda.synchronize()
+    # the gathered rows are the full sum of the same partials (the out-projection's, A)
+    out_rs_equal = bool(torch.equal(Yrs, A))
+    del Yrs
     rs_us = 1e3 * rs_ev[0].elapsed_time(rs_ev[1]) / rs_reps
     out["sequence_parallel"] = {
         "what": "reduce-scatter of the 70B y(t) partials: each of 8 ranks sums its 2048 token rows",
         "all_ranks_us": round(rs_us, 1), "per_rank_us": round(rs_us / T_p, 1),
         "gbs": round(psum_bytes / (rs_us * 1e-6) / 1e9, 1),
-        "full_partial_sum_us": round(avg_us["psum"], 1)}
+        "full_partial_sum_us": round(avg_us["psum"], 1),
+        "rows_equal_full_sum": out_rs_equal}
     log(f"[bench] reduce-scatter: 8 ranks {rs_us:.1f} us (full sum {avg_us['psum']:.1f} us)")
 
     if not args.no_backward:
@@ -575,6 +581,8 @@ def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
     e_y = O.normwise_max_rel_err(yg, y_ref)
     e_a = O.normwise_max_rel_err(ag, a_ref)
     log(f"[bench] oracle {cpu_s:.1f} s; max err ffn {e_y:.3e} attn {e_a:.3e}")
+    if not (e_y <= TOL and e_a <= TOL):
+        log(f"[bench] PARITY FAILURE: GPU results differ from the oracle beyond {TOL}")
     return {
         "cpu_baseline": {"value": round(flops / cpu_s / 1e12, 4), "unit": "TFLOP/s", "cores": cores,
                          "kind": "oracle", "seconds": round(cpu_s, 2),
