@@ -323,3 +323,50 @@ def test_outproj_backward_llama3_70b_shape_sampled():
     e2 = nerr(host64(dwo)[t * k + cols], f64(o[:, cols], w.dtype).T @ dy64)
     log(f"[outproj-bwd-full] dO {e1:.2e} dWo {e2:.2e}")
     assert e1 < BF16_TOL and e2 < BF16_TOL
+
+
+def test_new_entry_points_with_no_tokens():
+    """T = 0: the training forward and the reduce-scatter are no-ops; the out-projection
+    backward zeroes rank t's rows of dWo and touches nothing else."""
+    d, H, dh, T_p, t = 64, 8, 64, 4, 2
+    k = H // T_p * dh
+    z = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.full((8, d), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    S.tp_ffn_shard_fwd_train(z, z, None, z, y, z, z, None, 0, d, 256, T_p, t, "gelu", S.TP_BF16)
+    S.tp_reduce_scatter_rows(z, 0, T_p, t, None, y, 0, d, S.TP_BF16, S.TP_BF16)
+    dwo = torch.full((H * dh, d), SENTINEL, dtype=torch.float32, device="cuda:0")
+    S.tp_attn_outproj_shard_bwd(z, z, z, z, dwo, 0, d, H, H, dh, T_p, t, S.TP_F32)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    g = host64(dwo)
+    assert np.all(g[t * k:(t + 1) * k] == 0.0)
+    _check_untouched(g, t * k, (t + 1) * k, 0, "dWo")
+
+
+@pytest.mark.slow
+def test_backward_gpt2_medium_shape_every_rank():
+    """GELU workload at full size (4096 tokens, d 1024, d_ff 4096, TP4): every rank's dX(t) and
+    weight-gradient blocks against the oracle, and the reduced dX against the unsharded one."""
+    w = I.WORKLOADS[2]
+    T, d, d_ff, T_p, act = w.T, w.d, w.d_ff, w.T_p, w.act
+    n = d_ff // T_p
+    host = {k: I.make_tensor(w, k) for k in ("x", "w1", "w2", "dy")}
+    D = {k: dev(a, w.dtype) for k, a in host.items()}
+    x, w1, w2, dy = (f64(host[k], w.dtype) for k in ("x", "w1", "w2", "dy"))
+    parts = torch.empty((T_p, T, d), dtype=torch.float32, device="cuda:0")
+    for t in range(T_p):
+        b = t * n
+        _, h, u, v = _train_fwd(D["x"], D["w1"], None, D["w2"], T, d, d_ff, T_p, t, act)
+        dx, dw1, _, dw2 = _bwd(D["x"], D["w1"], None, D["w2"], D["dy"], h, u, v, T, d, d_ff, T_p, t, act,
+                               S.TP_F32, S.TP_F32)
+        parts[t].copy_(dx)
+        ref = O.ffn_shard_bwd(x, w1, None, w2, dy, T_p, t, act)
+        errs = (nerr(host64(dx), ref["dx_t"]), nerr(host64(dw1)[:, b:b + n], ref["dw1"]),
+                nerr(host64(dw2)[b:b + n, :], ref["dw2"]))
+        log(f"[bwd-gpt2] t={t} dx={errs[0]:.2e} dw1={errs[1]:.2e} dw2={errs[2]:.2e}")
+        assert max(errs) < BF16_TOL
+    dx_all = torch.empty((T, d), dtype=torch.float32, device="cuda:0")
+    S.tp_partial_sum(parts, T * d, T_p, None, dx_all, T * d, S.TP_F32, S.TP_F32)
+    torch.cuda.synchronize()
+    full = O.ffn_shard_bwd(x, w1, None, w2, dy, 1, 0, act)["dx_t"]
+    assert nerr(host64(dx_all), full) < BF16_TOL
