@@ -321,6 +321,49 @@ def attention_head(q, k, v, causal: bool = True, rows=None) -> np.ndarray:
     return p @ v
 
 
+def ring_attention_step(q, k, v, o_state, lse_state, q_pos0: int, k_pos0: int,
+                        causal: bool = True):
+    """Fold one K/V chunk into the running attention state of a query chunk (one head).
+
+    Context parallelism ("7.9 Tensor and pipeline parallelism" section 6; "Parallelism
+    II: model", "Sequence and context parallelism"; "Tensor & Pipeline Parallelism" (S17),
+    which passes the FlashAttention running state round a ring): the sequence is split
+    into chunks over the devices, each keeps its own queries and takes in every chunk's
+    keys and values in turn.  The running state of a query row is (O, lse): O the
+    softmax-weighted mean of the values of the keys seen so far, lse the natural log of
+    the softmax denominator over them (-inf and 0 before any key).  Positions: query row
+    i is at q_pos0 + i, key row k at k_pos0 + k; causal lets a query see keys at or
+    before its own position.  Returns the new (O, lse); rows that see no key of this
+    chunk keep their state unchanged.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o_state = np.asarray(o_state, dtype=np.float64)
+    lse_state = np.asarray(lse_state, dtype=np.float64)
+    dh = q.shape[1]
+    s = (q @ k.T) / math.sqrt(dh)
+    if causal:
+        qpos = q_pos0 + np.arange(q.shape[0])
+        kpos = k_pos0 + np.arange(k.shape[0])
+        s = np.where(kpos[None, :] > qpos[:, None], -np.inf, s)
+    seen = np.isfinite(s).any(axis=1)
+    # this chunk's own softmax over its visible keys
+    m = np.where(seen, np.max(np.where(np.isfinite(s), s, -np.inf), axis=1), 0.0)
+    e = np.exp(s - m[:, None])                 # exp(-inf) = 0 for masked keys
+    den = e.sum(axis=1)
+    lse_c = np.where(seen, m + np.log(np.where(seen, den, 1.0)), -np.inf)
+    o_c = (e @ v) / np.where(seen, den, 1.0)[:, None]
+    # merge: lse' = ln(e^lse + e^lse_c), O' = e^(lse - lse') O + e^(lse_c - lse') O_c
+    big = np.maximum(lse_state, lse_c)
+    big_f = np.where(np.isfinite(big), big, 0.0)
+    w_old = np.exp(lse_state - big_f)
+    w_new = np.exp(lse_c - big_f)
+    lse_new = big_f + np.log(np.where(seen, w_old + w_new, 1.0))
+    o_new = (w_old[:, None] * o_state + w_new[:, None] * o_c) / np.where(seen, w_old + w_new, 1.0)[:, None]
+    return np.where(seen[:, None], o_new, o_state), np.where(seen, lse_new, lse_state)
+
+
 def attn_heads_shard(x, wq, wk, wv, n_heads: int, n_kv_heads: int, head_dim: int, T_p: int,
                      t: int, causal: bool = True, rows=None, kv_replicate: bool = False) -> np.ndarray:
     """O(t): the rank's heads' outputs concatenated, [T (or len(rows)), h_t*head_dim].

@@ -12,6 +12,7 @@ import pytest
 
 import test_oracle_backward as bpins
 import test_oracle_pins as pins
+import test_oracle_ring as rpins
 from oracle import tp_oracle as O
 
 
@@ -112,6 +113,37 @@ def _dw2_from_preactivation(x, w1, w3, w2, dy, T_p, t, act):
     return g
 
 
+_orig_ring = O.ring_attention_step
+
+
+def _ring_chunk_alone(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal):
+    fresh = (np.zeros_like(np.asarray(o_state, dtype=np.float64)),
+             np.full_like(np.asarray(lse_state, dtype=np.float64), -np.inf))
+    return _orig_ring(q, k, v, *fresh, q_pos0, k_pos0, causal)
+
+
+def _ring_drops_old_state(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal=True):
+    """The chunk's result replaces the state instead of merging with it."""
+    o_c, l_c = _ring_chunk_alone(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal)
+    seen = np.isfinite(l_c)
+    return np.where(seen[:, None], o_c, o_state), np.where(seen, l_c, lse_state)
+
+
+def _ring_lse_max(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal=True):
+    """Keeps the larger log-denominator instead of the log of the summed weights."""
+    o_c, l_c = _ring_chunk_alone(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal)
+    seen = np.isfinite(l_c)
+    big = np.maximum(lse_state, l_c)
+    big_f = np.where(np.isfinite(big), big, 0.0)
+    o = np.exp(lse_state - big_f)[:, None] * o_state + np.exp(l_c - big_f)[:, None] * o_c
+    return np.where(seen[:, None], o, o_state), np.where(seen, big, lse_state)
+
+
+def _ring_masks_diagonal(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal=True):
+    """A query no longer sees the key at its own position."""
+    return _orig_ring(q, k, v, o_state, lse_state, q_pos0 - 1, k_pos0, causal)
+
+
 MUTATIONS = [
     ("silu", _wrong_silu_sign, [lambda: pins.test_silu_closed_forms_and_library(),
                                 lambda: pins.test_brute_force_tiny("swiglu", 2)]),
@@ -132,6 +164,12 @@ MUTATIONS = [
                                                 lambda: bpins.test_backward_matches_torch_autograd_fp64("swiglu", 4)]),
     ("ffn_shard_bwd", _dx_without_w3_term, [lambda: bpins.test_backward_matches_finite_differences("bilinear")]),
     ("ffn_shard_bwd", _dw2_from_preactivation, [lambda: bpins.test_backward_matches_torch_autograd_fp64("gelu", 4)]),
+    ("ring_attention_step", _ring_drops_old_state, [lambda: rpins.test_ring_equals_full_attention(2, True),
+                                                    lambda: rpins.test_ring_step_brute_force_tiny()]),
+    ("ring_attention_step", _ring_lse_max, [lambda: rpins.test_ring_zero_queries_closed_form(),
+                                            lambda: rpins.test_ring_equals_full_attention(3, False)]),
+    ("ring_attention_step", _ring_masks_diagonal, [lambda: rpins.test_ring_zero_queries_closed_form(),
+                                                   lambda: rpins.test_ring_equals_full_attention(4, True)]),
 ]
 
 
