@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TPSHARD_ABI_VERSION 2
+#define TPSHARD_ABI_VERSION 3
 
 /* Status codes. */
 #define TP_OK                 0
@@ -298,6 +298,62 @@ int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o,
                      int64_t n_seq, int64_t seq_len, int32_t h_t, int32_t kv_t,
                      int32_t head_dim, int64_t ldq, int64_t ldkv, int64_t ldo,
                      int32_t causal, void* hip_stream);
+
+/*
+ * Context parallelism (ring attention): "7.9 Tensor and pipeline parallelism",
+ * section 6; "Parallelism II: model", "Sequence and context parallelism"; and
+ * "Tensor & Pipeline Parallelism" (S17), which names passing the FlashAttention
+ * running state round a ring.  The sequence is split into chunks over the ranks of
+ * a context-parallel group; each rank keeps its query chunk and folds in the K/V
+ * chunks one at a time as they come round.  These three calls are one rank's
+ * share: set up the running state, fold one K/V chunk into it, and turn it into O.
+ *
+ * The running state of each query row r and local head j:
+ *   o_state[r, j*head_dim + c]  fp32, the softmax-weighted mean of the values of
+ *                               the keys folded in so far (0 before the first);
+ *   lse_state[r, j]             fp32, ln of the row's softmax denominator over
+ *                               those keys, sum_k exp(q.k / sqrt(head_dim))
+ *                               (-inf before the first).
+ * Folding chunk c into (O, lse) with the chunk's own (O_c, lse_c):
+ *   lse' = ln(e^lse + e^lse_c),  O' = e^(lse - lse') O + e^(lse_c - lse') O_c.
+ * Any order of chunks gives the same result up to rounding; after all of them O is
+ * softmax(Q K^T / sqrt(head_dim) [+ causal mask]) V over the whole sequence.
+ *
+ * tp_attn_ring_init: o_state[:, :h_t*head_dim] = 0, lse_state[:, :h_t] = -inf for
+ *   `rows` rows.  o_state 16-byte aligned, ld_state >= h_t*head_dim and a multiple
+ *   of 4; ld_lse >= h_t.
+ */
+int tp_attn_ring_init(void* o_state, void* lse_state, int64_t rows, int32_t h_t,
+                      int32_t head_dim, int64_t ld_state, int64_t ld_lse, void* hip_stream);
+
+/*
+ * tp_attn_ring_step: fold one K/V chunk into the running state of this rank's query
+ * chunk.  q, k, v as for tp_attn_core_fwd (n_seq sequences of seq_len rows each;
+ * every sequence is split the same way, so the query and key chunks have the same
+ * length).  q_pos0 / k_pos0: the position in the sequence of the chunks' first rows.
+ * Causal: query row i (position q_pos0 + i) sees key row k (position k_pos0 + k)
+ * when k_pos0 + k <= q_pos0 + i.  A query row that sees no key of this chunk keeps
+ * its state bit for bit, and a chunk that lies wholly after the query chunk is a
+ * no-op (nothing is launched).  The state is read and written in place (rows
+ * [0, n_seq*seq_len)); it must not overlap q, k or v.
+ * Errors: as tp_attn_core_fwd; TP_ERR_INVALID_ARG for negative positions or
+ * |q_pos0 - k_pos0| >= 2^30, or a misaligned / too narrow state.
+ */
+int tp_attn_ring_step(const void* q, const void* k, const void* v, void* o_state,
+                      void* lse_state, int64_t n_seq, int64_t seq_len, int32_t h_t,
+                      int32_t kv_t, int32_t head_dim, int64_t ldq, int64_t ldkv,
+                      int64_t ld_state, int64_t ld_lse, int64_t q_pos0, int64_t k_pos0,
+                      int32_t causal, void* hip_stream);
+
+/*
+ * tp_attn_ring_finish: o[:, :h_t*head_dim] = bf16(o_state[:, :h_t*head_dim]), round
+ * to nearest even, for `rows` rows.  ldo >= h_t*head_dim, a multiple of 4; o 16-byte
+ * aligned and not overlapping the state.  After every chunk has been folded in, o
+ * equals what tp_attn_core_fwd writes for the whole sequence (up to rounding; with a
+ * single chunk, bit for bit).
+ */
+int tp_attn_ring_finish(const void* o_state, void* o, int64_t rows, int32_t h_t,
+                        int32_t head_dim, int64_t ld_state, int64_t ldo, void* hip_stream);
 
 /*
  * Local partial sum standing in for the all-reduce ("7.9 Tensor and

@@ -72,7 +72,8 @@ struct Flag {
 
 constexpr float kLazy = 8.0f;  // log2 of the largest exponential kept before rescaling
 
-template <int DH>
+// RING: fold the keys into the running state (o_state, lse_state) instead of writing O.
+template <int DH, bool RING>
 __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int nqb, int strands) {
   constexpr int CPR = DH / 8;           // 16-byte chunks per row
   constexpr int ROWB = DH * 2;          // bytes per row
@@ -123,6 +124,9 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
 
   // ---- Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
   const int qrow = q0 + 32 * qh + (lane & 31);
+  // Ring step: this row's log-denominator so far, read before any wave can overwrite it
+  float lse_old = -INFINITY;
+  if (RING && qrow < S) lse_old = a.lse_state[(row0 + qrow) * a.ld_lse + j];
   bf16x8 qf[KS];
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -156,7 +160,9 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
   const uint32_t v_off0 = (uint32_t)(c_row0 * a.ldkv + 8 * (c_slot ^ (swz_v(c_row0) & (CPR - 1)))) * 2u;
   const uint32_t copy_step = (uint32_t)(RPC * a.ldkv) * 2u;
   static_assert(RPC % 4 == 0, "V swizzle period");
-  const int kend = a.causal ? (q0 + kBQ < S ? q0 + kBQ : S) : S;
+  // keys this block needs: causal stops after the last query's position
+  const int kend = a.causal ? (q0 + kBQ + a.delta < S ? q0 + kBQ + a.delta : S) : S;
+  if (RING && kend <= 0) return;   // every key lies after every query: the state stands
   const int nkb = (kend + kBK - 1) / kBK;
   const int nit = (nkb + kGroups - 1) / kGroups;   // same for every wave
 
@@ -204,7 +210,7 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
   // Does block `it` of this group reach past the sequence or the diagonal?
   auto needs_mask = [&](int it) {
     const int key0 = (g + kGroups * it) * kBK;
-    return key0 + kBK > S || (a.causal && key0 + kBK - 1 > qmin);
+    return key0 + kBK > S || (a.causal && key0 + kBK - 1 > qmin + a.delta);
   };
   auto read_k = [&](const LDS_AS unsigned char* Ks, bf16x8 (&kf)[KS]) {
 #pragma unroll
@@ -243,7 +249,7 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (key >= S || (a.causal && key > qrow)) s[r] = -INFINITY;
+        if (key >= S || (a.causal && key > qrow + a.delta)) s[r] = -INFINITY;
       }
     }
     float mx = s[0];
@@ -385,8 +391,31 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
             for (int i = 0; i < 4; ++i) acc[4 * r4 + i] += al[h] * t[i];
           }
         }
-      // O = O^T / l, one 8-byte store per 4 consecutive head dims
-      if (qrow < S) {
+      if constexpr (RING) {
+        // Merge (O_c = acc / L, lse_c = ln L + Mu ln 2) into the state: with
+        // M = max(lse_old, lse_c) the weights are e^(lse - M), the new state the weighted
+        // mean of the two outputs and M + ln(sum of weights).  A row with no visible key
+        // in this chunk (L = 0) keeps its state.
+        if (qrow < S && L > 0.0f) {
+          constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+          const float lc = Mu + __builtin_amdgcn_logf(L);   // log2 units
+          const float lo = lse_old * kLog2e;
+          const float M2 = fmaxf(lo, lc);
+          const float w_o = __builtin_amdgcn_exp2f(lo - M2), w_c = __builtin_amdgcn_exp2f(lc - M2);
+          const float den = w_o + w_c;
+          const float r_o = w_o / den, r_c = w_c * inv / den;
+          float* St = a.o_state + (row0 + qrow) * a.ld_state + (int64_t)j * DH + 32 * d;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4* sp = (f32x4*)(St + 8 * r4 + 4 * (lane >> 5));
+            const f32x4 prev = *sp;
+            *sp = f32x4{r_o * prev[0] + r_c * acc[4 * r4], r_o * prev[1] + r_c * acc[4 * r4 + 1],
+                        r_o * prev[2] + r_c * acc[4 * r4 + 2], r_o * prev[3] + r_c * acc[4 * r4 + 3]};
+          }
+          if (g == 0) a.lse_state[(row0 + qrow) * a.ld_lse + j] = (M2 + __builtin_amdgcn_logf(den)) * kLn2;
+        }
+      } else if (qrow < S) {
+        // O = O^T / l, one 8-byte store per 4 consecutive head dims
         __bf16* Op = a.o + (row0 + qrow) * a.ldo + (int64_t)j * DH + 32 * d;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
@@ -407,12 +436,72 @@ hipError_t launch_attention(const AttnDesc& a, hipStream_t s) {
   int g8 = 8;
   while (a.h_t % g8) g8 >>= 1;   // gcd(h_t, 8)
   const int strands = nqb % (8 / g8) == 0 ? 8 / g8 : 0;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
+  const bool ring = a.o == nullptr;
+  if (ring && (a.o_state == nullptr || a.lse_state == nullptr)) return hipErrorInvalidValue;
+  if (a.head_dim == 128 && !ring)
+    hipLaunchKernelGGL((attention_kernel<128, false>), grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
+  else if (a.head_dim == 64 && !ring)
+    hipLaunchKernelGGL((attention_kernel<64, false>), grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((attention_kernel<128, true>), grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
   else if (a.head_dim == 64)
-    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
+    hipLaunchKernelGGL((attention_kernel<64, true>), grid, dim3(kWaves * 64), 0, s, a, (int)nqb, strands);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+namespace {
+
+// Ring state set-up: one thread per 4 columns of a row (cols a multiple of 4), and the
+// first `heads` threads of a row also clear its log-denominators.
+__global__ void ring_init_kernel(float* o_state, float* lse_state, int64_t rows, int32_t cols,
+                                 int32_t heads, int32_t ld_state, int32_t ld_lse) {
+  const int64_t row = blockIdx.y + (int64_t)gridDim.y * blockIdx.z;
+  if (row >= rows) return;
+  const int c = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (4 * c < cols) *(f32x4*)(o_state + row * ld_state + 4 * c) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (c < heads) lse_state[row * ld_lse + c] = -INFINITY;
+}
+
+// O = bf16(state), round to nearest even, 4 columns per thread
+__global__ void ring_finish_kernel(const float* o_state, __bf16* o, int64_t rows, int32_t cols,
+                                   int32_t ld_state, int32_t ldo) {
+  const int64_t row = blockIdx.y + (int64_t)gridDim.y * blockIdx.z;
+  const int c = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (row >= rows || 4 * c >= cols) return;
+  const f32x4 v = *(const f32x4*)(o_state + row * ld_state + 4 * c);
+  *(bf16x4*)(o + row * ldo + 4 * c) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
+// rows -> (y, z) grid dimensions within the 65535 limit of each
+bool row_grid(int64_t rows, int32_t cols, dim3& grid) {
+  const int64_t bx = (cols / 4 + 255) / 256;
+  const int64_t gy = rows < 65535 ? rows : 65535;
+  const int64_t gz = (rows + gy - 1) / gy;
+  if (bx > 0x7FFFFFFF || gz > 65535) return false;
+  grid = dim3((unsigned)(bx > 0 ? bx : 1), (unsigned)gy, (unsigned)gz);
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_ring_init(float* o_state, float* lse_state, int64_t rows, int32_t cols,
+                            int32_t heads, int32_t ld_state, int32_t ld_lse, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid;
+  if (cols % 4 || 4 * heads > cols || !row_grid(rows, cols, grid)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ring_init_kernel, grid, dim3(256), 0, s, o_state, lse_state, rows, cols, heads,
+                     ld_state, ld_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_finish(const float* o_state, __bf16* o, int64_t rows, int32_t cols,
+                              int32_t ld_state, int32_t ldo, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid;
+  if (cols % 4 || !row_grid(rows, cols, grid)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ring_finish_kernel, grid, dim3(256), 0, s, o_state, o, rows, cols, ld_state, ldo);
   return hipGetLastError();
 }
 

@@ -569,10 +569,14 @@ int tp_attn_heads_shard_fwd_kvrep(const void* x, const void* wq, const void* wk,
                          causal, hip_stream);
 }
 
-int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64_t n_seq,
-                     int64_t seq_len, int32_t h_t, int32_t kv_t, int32_t head_dim, int64_t ldq,
-                     int64_t ldkv, int64_t ldo, int32_t causal, void* hip_stream) {
-  const char* fn = "tp_attn_core_fwd";
+}  // extern "C"
+
+namespace {
+// The argument checks shared by the attention core and the ring step (everything but
+// the output / state).
+int check_core_args(const char* fn, const void* q, const void* k, const void* v, int64_t n_seq,
+                    int64_t seq_len, int32_t h_t, int32_t kv_t, int32_t head_dim, int64_t ldq,
+                    int64_t ldkv, int32_t causal) {
   if (n_seq < 0 || seq_len < 0 || n_seq > 65535 || seq_len > 0x7FFFFFFF)
     return fail(TP_ERR_INVALID_ARG, "%s: n_seq / seq_len out of range", fn);
   if (h_t <= 0 || kv_t <= 0 || h_t % kv_t || h_t > 65535)
@@ -580,9 +584,9 @@ int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64
   if (head_dim != 64 && head_dim != 128)
     return fail(TP_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", fn, head_dim);
   if (causal != 0 && causal != 1) return fail(TP_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
-  if (ldq < (int64_t)h_t * head_dim || ldo < (int64_t)h_t * head_dim || ldkv < (int64_t)kv_t * head_dim)
+  if (ldq < (int64_t)h_t * head_dim || ldkv < (int64_t)kv_t * head_dim)
     return fail(TP_ERR_INVALID_ARG, "%s: leading dimension smaller than the heads it holds", fn);
-  if (ldq % 8 || ldkv % 8 || ldo % 8 || ldq > kMaxExtent || ldkv > kMaxExtent || ldo > kMaxExtent)
+  if (ldq % 8 || ldkv % 8 || ldq > kMaxExtent || ldkv > kMaxExtent)
     return fail(TP_ERR_UNSUPPORTED, "%s: leading dimensions must be multiples of 8 and at most %lld", fn,
                 (long long)kMaxExtent);
   if ((int64_t)seq_len * (ldq > ldkv ? ldq : ldkv) * 2 >= (int64_t(1) << 30))
@@ -590,6 +594,42 @@ int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(v, "v"));
+  return TP_OK;
+}
+
+// Checks of a [rows, ld] fp32 ring state holding `cols` columns, and of its [rows, ld_lse]
+// log-denominators holding `heads` columns.
+int check_ring_state(const char* fn, const void* o_state, const void* lse_state, int32_t cols,
+                     int32_t heads, int64_t ld_state, int64_t ld_lse) {
+  if (ld_state < cols || ld_state % 4 || ld_state > kMaxExtent)
+    return fail(TP_ERR_INVALID_ARG, "%s: ld_state=%lld must be >= %d, a multiple of 4, at most %lld", fn,
+                (long long)ld_state, cols, (long long)kMaxExtent);
+  if (ld_lse < heads || ld_lse > kMaxExtent)
+    return fail(TP_ERR_INVALID_ARG, "%s: ld_lse=%lld must be >= h_t=%d and at most %lld", fn,
+                (long long)ld_lse, heads, (long long)kMaxExtent);
+  TRY(check_ptr(o_state, "o_state"));
+  if (lse_state) TRY(check_ptr(lse_state, "lse_state"));
+  return TP_OK;
+}
+
+bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a_bytes && b_bytes && a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+}  // namespace
+
+extern "C" {
+
+int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64_t n_seq,
+                     int64_t seq_len, int32_t h_t, int32_t kv_t, int32_t head_dim, int64_t ldq,
+                     int64_t ldkv, int64_t ldo, int32_t causal, void* hip_stream) {
+  const char* fn = "tp_attn_core_fwd";
+  TRY(check_core_args(fn, q, k, v, n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv, causal));
+  if (ldo < (int64_t)h_t * head_dim)
+    return fail(TP_ERR_INVALID_ARG, "%s: leading dimension smaller than the heads it holds", fn);
+  if (ldo % 8 || ldo > kMaxExtent)
+    return fail(TP_ERR_UNSUPPORTED, "%s: leading dimensions must be multiples of 8 and at most %lld", fn,
+                (long long)kMaxExtent);
   TRY(check_ptr(o, "o"));
   if (n_seq * seq_len == 0) return TP_OK;
   tpk::AttnDesc a{};
@@ -607,6 +647,96 @@ int tp_attn_core_fwd(const void* q, const void* k, const void* v, void* o, int64
   a.ldo = (int32_t)ldo;
   a.causal = causal != 0;
   return hip_status(tpk::launch_attention(a, (hipStream_t)hip_stream), "attention launch");
+}
+
+int tp_attn_ring_init(void* o_state, void* lse_state, int64_t rows, int32_t h_t, int32_t head_dim,
+                      int64_t ld_state, int64_t ld_lse, void* hip_stream) {
+  const char* fn = "tp_attn_ring_init";
+  if (rows < 0 || rows > kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: rows out of range", fn);
+  if (h_t <= 0 || h_t > 65535) return fail(TP_ERR_INVALID_ARG, "%s: h_t=%d out of range", fn, h_t);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TP_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", fn, head_dim);
+  const int64_t cols = (int64_t)h_t * head_dim;
+  if (cols > kMaxExtent) return fail(TP_ERR_UNSUPPORTED, "%s: h_t*head_dim too large", fn);
+  TRY(check_ptr(lse_state, "lse_state"));
+  TRY(check_ring_state(fn, o_state, lse_state, (int32_t)cols, h_t, ld_state, ld_lse));
+  if (overlaps(o_state, (size_t)(rows ? (rows - 1) * ld_state + cols : 0) * 4, lse_state,
+               (size_t)(rows ? (rows - 1) * ld_lse + h_t : 0) * 4))
+    return fail(TP_ERR_INVALID_ARG, "%s: o_state and lse_state overlap", fn);
+  return hip_status(tpk::launch_ring_init((float*)o_state, (float*)lse_state, rows, (int32_t)cols, h_t,
+                                          (int32_t)ld_state, (int32_t)ld_lse, (hipStream_t)hip_stream),
+                    "ring-init launch");
+}
+
+int tp_attn_ring_step(const void* q, const void* k, const void* v, void* o_state, void* lse_state,
+                      int64_t n_seq, int64_t seq_len, int32_t h_t, int32_t kv_t, int32_t head_dim,
+                      int64_t ldq, int64_t ldkv, int64_t ld_state, int64_t ld_lse, int64_t q_pos0,
+                      int64_t k_pos0, int32_t causal, void* hip_stream) {
+  const char* fn = "tp_attn_ring_step";
+  TRY(check_core_args(fn, q, k, v, n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv, causal));
+  TRY(check_ptr(lse_state, "lse_state"));
+  TRY(check_ring_state(fn, o_state, lse_state, h_t * head_dim, h_t, ld_state, ld_lse));
+  if (q_pos0 < 0 || k_pos0 < 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: negative chunk position", fn);
+  const int64_t delta = q_pos0 - k_pos0;
+  if (delta >= (int64_t(1) << 30) || delta <= -(int64_t(1) << 30))
+    return fail(TP_ERR_INVALID_ARG, "%s: |q_pos0 - k_pos0| must be below 2^30", fn);
+  const int64_t rows = n_seq * seq_len;
+  const size_t st_bytes = (size_t)(rows ? (rows - 1) * ld_state + h_t * head_dim : 0) * 4;
+  const size_t lse_bytes = (size_t)(rows ? (rows - 1) * ld_lse + h_t : 0) * 4;
+  const size_t q_bytes = (size_t)(rows ? (rows - 1) * ldq + h_t * head_dim : 0) * 2;
+  const size_t kv_bytes = (size_t)(rows ? (rows - 1) * ldkv + kv_t * head_dim : 0) * 2;
+  if (overlaps(o_state, st_bytes, lse_state, lse_bytes))
+    return fail(TP_ERR_INVALID_ARG, "%s: o_state and lse_state overlap", fn);
+  const void* ins[3] = {q, k, v};
+  const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(o_state, st_bytes, ins[i], in_bytes[i]) || overlaps(lse_state, lse_bytes, ins[i], in_bytes[i]))
+      return fail(TP_ERR_INVALID_ARG, "%s: the state overlaps q, k or v", fn);
+  if (rows == 0) return TP_OK;
+  // the whole key chunk comes after the whole query chunk: nothing to fold in
+  if (causal && k_pos0 > q_pos0 + seq_len - 1) return TP_OK;
+  tpk::AttnDesc a{};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.o = nullptr;
+  a.n_seq = n_seq;
+  a.seq_len = (int32_t)seq_len;
+  a.head_dim = head_dim;
+  a.h_t = h_t;
+  a.kv_t = kv_t;
+  a.ldq = (int32_t)ldq;
+  a.ldkv = (int32_t)ldkv;
+  a.causal = causal != 0;
+  a.delta = (int32_t)delta;
+  a.o_state = (float*)o_state;
+  a.lse_state = (float*)lse_state;
+  a.ld_state = (int32_t)ld_state;
+  a.ld_lse = (int32_t)ld_lse;
+  return hip_status(tpk::launch_attention(a, (hipStream_t)hip_stream), "ring-step launch");
+}
+
+int tp_attn_ring_finish(const void* o_state, void* o, int64_t rows, int32_t h_t, int32_t head_dim,
+                        int64_t ld_state, int64_t ldo, void* hip_stream) {
+  const char* fn = "tp_attn_ring_finish";
+  if (rows < 0 || rows > kMaxRows) return fail(TP_ERR_INVALID_ARG, "%s: rows out of range", fn);
+  if (h_t <= 0 || h_t > 65535) return fail(TP_ERR_INVALID_ARG, "%s: h_t=%d out of range", fn, h_t);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TP_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", fn, head_dim);
+  const int64_t cols = (int64_t)h_t * head_dim;
+  if (cols > kMaxExtent) return fail(TP_ERR_UNSUPPORTED, "%s: h_t*head_dim too large", fn);
+  TRY(check_ring_state(fn, o_state, nullptr, (int32_t)cols, h_t, ld_state, h_t));
+  if (ldo < cols || ldo % 4 || ldo > kMaxExtent)
+    return fail(TP_ERR_INVALID_ARG, "%s: ldo=%lld must be >= %lld, a multiple of 4, at most %lld", fn,
+                (long long)ldo, (long long)cols, (long long)kMaxExtent);
+  TRY(check_ptr(o, "o"));
+  if (overlaps(o_state, (size_t)(rows ? (rows - 1) * ld_state + cols : 0) * 4, o,
+               (size_t)(rows ? (rows - 1) * ldo + cols : 0) * 2))
+    return fail(TP_ERR_INVALID_ARG, "%s: o overlaps the state", fn);
+  return hip_status(tpk::launch_ring_finish((const float*)o_state, (__bf16*)o, rows, (int32_t)cols,
+                                            (int32_t)ld_state, (int32_t)ldo, (hipStream_t)hip_stream),
+                    "ring-finish launch");
 }
 
 int tp_partial_sum(const void* partials, int64_t partial_stride, int32_t T_p, const void* residual,

@@ -69,7 +69,23 @@ struct AttnDesc {
   int32_t seq_len, head_dim, h_t, kv_t;
   int32_t ldq, ldkv, ldo;
   bool causal;
+  // Causal masking by position: query row i sees key row k when k <= i + delta (delta =
+  // position of the first query minus that of the first key; 0 within one sequence).
+  int32_t delta;
+  // Ring step (o == nullptr): fold this K/V chunk into the running state instead of
+  // writing O.  o_state [n_seq*seq_len, ld_state] fp32 holds the normalised output so far,
+  // lse_state [n_seq*seq_len, ld_lse] fp32 the natural log of each row's softmax
+  // denominator (-inf: no key seen yet).
+  float* o_state;
+  float* lse_state;
+  int32_t ld_state, ld_lse;
 };
 hipError_t launch_attention(const AttnDesc& a, hipStream_t s);
+// o_state[:, :h_t*head_dim] = 0 and lse_state[:, :h_t] = -inf for `rows` rows
+hipError_t launch_ring_init(float* o_state, float* lse_state, int64_t rows, int32_t cols,
+                            int32_t heads, int32_t ld_state, int32_t ld_lse, hipStream_t s);
+// o[:, :cols] = bf16(o_state[:, :cols]) for `rows` rows (cols a multiple of 4)
+hipError_t launch_ring_finish(const float* o_state, __bf16* o, int64_t rows, int32_t cols,
+                              int32_t ld_state, int32_t ldo, hipStream_t s);
 
 }  // namespace tpk

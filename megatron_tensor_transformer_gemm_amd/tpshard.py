@@ -62,6 +62,10 @@ _SIGS = {
     "tp_reduce_scatter_rows": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i64, _i32, _i32, _vp]),
     "tp_ffn_shard_bwd": (_i32, [_vp] * 12 + [_vp, _sz, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                              _vp]),
+    "tp_attn_ring_init": (_i32, [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]),
+    "tp_attn_ring_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _i64,
+                                 _i64, _i64, _i64, _i64, _i32, _vp]),
+    "tp_attn_ring_finish": (_i32, [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]),
 }
 
 _lib = None
@@ -199,6 +203,23 @@ def tp_attn_core_fwd(q, k, v, o, n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv,
     _check("tp_attn_core_fwd", lib().tp_attn_core_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv, ldo,
         int(causal), _stream(hip_stream)))
+
+
+def tp_attn_ring_init(o_state, lse_state, rows, h_t, head_dim, ld_state, ld_lse, hip_stream=None):
+    _check("tp_attn_ring_init", lib().tp_attn_ring_init(
+        _ptr(o_state), _ptr(lse_state), rows, h_t, head_dim, ld_state, ld_lse, _stream(hip_stream)))
+
+
+def tp_attn_ring_step(q, k, v, o_state, lse_state, n_seq, seq_len, h_t, kv_t, head_dim, ldq, ldkv,
+                      ld_state, ld_lse, q_pos0, k_pos0, causal, hip_stream=None):
+    _check("tp_attn_ring_step", lib().tp_attn_ring_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o_state), _ptr(lse_state), n_seq, seq_len, h_t, kv_t,
+        head_dim, ldq, ldkv, ld_state, ld_lse, q_pos0, k_pos0, int(causal), _stream(hip_stream)))
+
+
+def tp_attn_ring_finish(o_state, o, rows, h_t, head_dim, ld_state, ldo, hip_stream=None):
+    _check("tp_attn_ring_finish", lib().tp_attn_ring_finish(
+        _ptr(o_state), _ptr(o), rows, h_t, head_dim, ld_state, ldo, _stream(hip_stream)))
 
 
 def tp_partial_sum(partials, partial_stride, T_p, residual, y, n_elems, part_dtype, out_dtype,

@@ -22,10 +22,10 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 19
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
-    assert S.tp_abi_version() == 2
+    assert S.tp_abi_version() == 3
 
 
 @pytest.mark.parametrize("extent,T_p", [(14336, 8), (28672, 8), (4096, 4), (27720, 11), (0, 3),
@@ -244,4 +244,71 @@ def test_kvrep_rejects_before_launch(kw, code):
     a.update(kw)
     with pytest.raises(S.TPError) as e:
         S.tp_attn_heads_shard_fwd_kvrep(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+_RING = dict(q=P, k=P + (1 << 24), v=P + (2 << 24), o_state=P + (3 << 24), lse_state=P + (5 << 24),
+             n_seq=1, seq_len=256, h_t=4, kv_t=2, head_dim=128, ldq=512, ldkv=256, ld_state=512,
+             ld_lse=4, q_pos0=256, k_pos0=0, causal=True, hip_stream=0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ld_state=510), S.TP_ERR_INVALID_ARG),        # not a multiple of 4
+    (dict(ld_state=256), S.TP_ERR_INVALID_ARG),        # narrower than h_t*head_dim
+    (dict(ld_lse=3), S.TP_ERR_INVALID_ARG),            # narrower than h_t
+    (dict(q_pos0=-1), S.TP_ERR_INVALID_ARG),
+    (dict(q_pos0=1 << 30, k_pos0=0), S.TP_ERR_INVALID_ARG),
+    (dict(head_dim=96, ldq=384, ldkv=192, ld_state=384), S.TP_ERR_UNSUPPORTED),
+    (dict(lse_state=None), S.TP_ERR_INVALID_ARG),
+    (dict(o_state=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(o_state=P), S.TP_ERR_INVALID_ARG),           # the state overlaps q
+    (dict(lse_state=P + (3 << 24)), S.TP_ERR_INVALID_ARG),   # lse overlaps o_state
+    (dict(h_t=3), S.TP_ERR_INVALID_ARG),               # not a multiple of kv_t
+    (dict(causal=2), S.TP_ERR_INVALID_ARG),
+])
+def test_ring_step_rejects_before_launch(kw, code):
+    a = dict(_RING)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_ring_step(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+def test_ring_step_without_work_launches_nothing():
+    """A key chunk wholly after the query chunk (causal), or an empty chunk, returns before
+    any launch, so fake device addresses are fine."""
+    S.tp_attn_ring_step(**dict(_RING, q_pos0=0, k_pos0=256))
+    S.tp_attn_ring_step(**dict(_RING, q_pos0=0, k_pos0=10_000))
+    S.tp_attn_ring_step(**dict(_RING, seq_len=0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ld_state=510), S.TP_ERR_INVALID_ARG),
+    (dict(ld_lse=3), S.TP_ERR_INVALID_ARG),
+    (dict(rows=-1), S.TP_ERR_INVALID_ARG),
+    (dict(head_dim=32), S.TP_ERR_UNSUPPORTED),
+    (dict(lse_state=P + 64), S.TP_ERR_INVALID_ARG),    # overlaps o_state
+])
+def test_ring_init_rejects_before_launch(kw, code):
+    a = dict(o_state=P, lse_state=P + (1 << 24), rows=256, h_t=4, head_dim=128, ld_state=512, ld_lse=4,
+             hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_ring_init(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ldo=510), S.TP_ERR_INVALID_ARG),
+    (dict(ldo=256), S.TP_ERR_INVALID_ARG),
+    (dict(o=P + 1024), S.TP_ERR_INVALID_ARG),          # overlaps the state
+    (dict(o=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(h_t=0), S.TP_ERR_INVALID_ARG),
+])
+def test_ring_finish_rejects_before_launch(kw, code):
+    a = dict(o_state=P, o=P + (1 << 24), rows=256, h_t=4, head_dim=128, ld_state=512, ldo=512,
+             hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_attn_ring_finish(**a)
     assert e.value.code == code, S.tp_last_error()
