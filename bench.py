@@ -82,6 +82,8 @@ def main() -> int:
                     help="skip the extra GPT-style block measurement (attention core)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the extra measurement of the FFN shard backward")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the extra measurement of ring attention (context parallelism)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="read the rocprofv3 counter_collection.csv files of two --pmc-pass "
                          "runs (FETCH_SIZE, WRITE_SIZE), write profiles/hbm_traffic.json, exit")
@@ -294,6 +296,8 @@ def main() -> int:
         out["backward"] = measure_backward(w, X, W1, W3, W2, max(2, args.steps // 4), 1)
     if not args.no_block:
         out["block_workload"] = measure_block(max(2, args.steps // 4), 1)
+    if not args.no_ring:
+        out["context_parallel_ring"] = measure_ring(max(2, args.steps // 4), 1)
     if not args.no_cpu_baseline:
         out.update(cpu_baseline(host, w, Y, A, args.cpu_rows))
     else:
@@ -539,6 +543,68 @@ def measure_block(steps: int, warmup: int) -> dict:
     }
     log(f"[bench] block: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; attention core {core_us:.1f} us")
     return res
+
+
+def measure_ring(steps: int, warmup: int) -> dict:
+    """Context parallelism on one GPU: a rank's 6 heads of 128 (the GPT block's TP8 share)
+    over one causal 8192-token sequence split into 4 chunks of 2048.  Every CP rank r sets
+    up its running state, folds in K/V chunks r, r-1, ..., 0 (the later ones lie after its
+    queries and are skipped), and writes O.  Reported: the four ranks' ring work against
+    one attention-core call on the whole sequence (same causal FLOPs), the most loaded
+    rank alone (its time is the group's critical path when each rank has a GPU), and the
+    normwise difference of the two outputs."""
+    import torch
+
+    from megatron_tensor_transformer_gemm_amd import tpshard as S
+
+    L, C, h_t, dh = 8192, 4, 6, 128
+    c, kd = L // C, h_t * dh
+    g = torch.Generator(device="cuda").manual_seed(11)
+    q, k, v = (torch.randn(L, kd, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    o_full = torch.empty(L, kd, dtype=torch.bfloat16, device="cuda")
+    o_ring = torch.empty(L, kd, dtype=torch.bfloat16, device="cuda")
+    st = [torch.empty(c, kd, dtype=torch.float32, device="cuda") for _ in range(C)]
+    lse = [torch.empty(c, h_t + 2, dtype=torch.float32, device="cuda") for _ in range(C)]
+
+    def full():
+        S.tp_attn_core_fwd(q, k, v, o_full, 1, L, h_t, h_t, dh, kd, kd, kd, True)
+
+    def ring(ranks=range(C)):
+        for r in ranks:
+            S.tp_attn_ring_init(st[r], lse[r], c, h_t, dh, kd, h_t + 2)
+            for s_ in range(C):
+                src = (r - s_) % C
+                S.tp_attn_ring_step(q[r * c:], k[src * c:], v[src * c:], st[r], lse[r], 1, c, h_t, h_t,
+                                    dh, kd, kd, kd, h_t + 2, r * c, src * c, True)
+            S.tp_attn_ring_finish(st[r], o_ring[r * c:], c, h_t, dh, kd, kd)
+
+    def timed(fn):
+        for _ in range(warmup + 1):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / steps
+
+    full_us = timed(full)
+    last_us = timed(lambda: ring([C - 1]))     # the most loaded rank: every chunk is visible
+    ring_us = timed(ring)
+    diff = float((o_ring.float() - o_full.float()).abs().max() / o_full.float().abs().max())
+    fl = 2.0 * h_t * dh * L * (L + 1)
+    log(f"[bench] ring attention: 4 CP ranks {ring_us:.1f} us (last rank {last_us:.1f} us) vs whole "
+        f"sequence {full_us:.1f} us, max_err {diff:.2e}")
+    if diff > 2e-2:
+        log(f"[bench] PARITY FAILURE: ring attention differs from the whole-sequence core by {diff:.3e}")
+    return {"what": "causal 8192-token sequence, 6 heads of 128, 4 context-parallel chunks of 2048: "
+                    "all ranks' ring steps (init, 10 chunk folds, finish) vs one whole-sequence core call",
+            "ring_all_ranks_us": round(ring_us, 1), "whole_sequence_us": round(full_us, 1),
+            "last_rank_us": round(last_us, 1),
+            "ring_tflops": round(fl / (ring_us * 1e-6) / 1e12, 1),
+            "whole_tflops": round(fl / (full_us * 1e-6) / 1e12, 1),
+            "max_err_vs_whole": diff}
 
 
 def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
