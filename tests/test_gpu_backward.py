@@ -56,8 +56,8 @@ def _check_untouched(full: np.ndarray, lo: int, hi: int, axis: int, name: str):
 
 # ----------------------------------------------------------------------------- bit-exact offsets
 @pytest.mark.parametrize("act", ["none", "bilinear"])
-@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (4100, 1032, 2, 1288)],
-                         ids=["small-tiles", "large-tiles"])
+@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (4100, 1032, 2, 1288), (4100, 264, 1, 4000)],
+                         ids=["small-tiles", "large-tiles", "dH-128x256-3-stage"])
 def test_backward_integer_bit_exact(act, shape):
     """Integer inputs: dX(t) and the weight-gradient blocks (fp32) equal the oracle bit for bit,
     and nothing outside the rank's blocks is written."""
