@@ -29,6 +29,12 @@
 // the sequence come back as zeros and are masked to -inf.  At the end the four groups'
 // partial states (m, l, O^T) meet in LDS: wave (g, half) rescales and sums the four
 // partials of head-dimension block g of its 32 queries and stores it.
+//
+// Ring step (context parallelism: "7.9 Tensor and pipeline parallelism" section 6,
+// "Tensor & Pipeline Parallelism" (S17) "Sequence / ring attention"): the same kernel with
+// a position offset between the query and key chunks (causal masking compares positions)
+// and an epilogue that merges the chunk's normalised output and log-denominator into a
+// running fp32 state instead of writing O.
 #include "tp_internal.h"
 #include "lds_copy.h"
 
