@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_SCLK_MHZ = 2400          # the shader clock that peak assumes
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TOL = 2e-2                    # normwise max relative error, bf16 with fp32 accumulation
 PSUM_PAD = 2048               # elements between partial slices (4 KiB of bf16)
@@ -68,6 +69,60 @@ def load_traffic(kernel: str, workload: str, per_launch_units: float):
     if not ent or ent.get("source_digest") != kernel_source_digest():
         return None
     return ent.get("bytes_per_launch")
+
+
+class SclkSampler:
+    """Samples the shader clock from a host thread while the GPU works: the current DPM
+    level (the line marked '*') of the card's pp_dpm_sclk, every `period_s` seconds.
+    Reports nothing when there is not exactly one card or the file cannot be read."""
+
+    def __init__(self, period_s: float = 0.01):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if len(paths) == 1 else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "samples": len(v),
+                "source": "current DPM level in pp_dpm_sclk, sampled every "
+                          f"{int(self.period * 1e3)} ms over the timed steps"}
 
 
 def main() -> int:
@@ -202,11 +257,13 @@ def main() -> int:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    with SclkSampler() as sclk_sampler:
+        t_start = time.perf_counter()
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    sclk = sclk_sampler.summary()
     ms_per_step = elapsed * 1e3 / args.steps
 
     dur = {}  # kernel name -> list of ms
@@ -250,6 +307,12 @@ def main() -> int:
                 "traffic": load_traffic("column_gemm_swiglu", w.name, fl_col),
                 "kernel": "column-parallel GEMM + SwiGLU epilogue (per rank)",
                 "flops_per_launch": fl_col}
+    if sclk:
+        # the same kernel against the MFMA rate at the clock the power manager set
+        roofline["frac_at_measured_sclk"] = round(
+            col_tf / (PEAK_BF16_TFLOPS * sclk["median_mhz"] / PEAK_SCLK_MHZ), 4)
+        log(f"[bench] shader clock over the timed steps: median {sclk['median_mhz']} MHz "
+            f"({sclk['min_mhz']}-{sclk['max_mhz']}, {sclk['samples']} samples)")
 
     out = {
         "metric": "TP-shard FFN fwd TFLOP/s (bf16, 1 GPU) + % of MFMA peak; oracle-match max err",
@@ -264,6 +327,7 @@ def main() -> int:
         "step_gemm_flops": step_flops,
         "kernels": kernels,
         "roofline": roofline,
+        "sclk": sclk,
     }
 
     # sequence-parallel form of the same reduce: 8 ranks' row slices (reduce-scatter), into
