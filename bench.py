@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_SCLK_MHZ = 2400          # the shader clock that peak assumes
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TOL = 2e-2                    # normwise max relative error, bf16 with fp32 accumulation
 PSUM_PAD = 2048               # elements between partial slices (4 KiB of bf16)
@@ -139,6 +140,8 @@ def main() -> int:
                     help="skip the extra measurement of the FFN shard backward")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the extra measurement of ring attention (context parallelism)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the extra measurement of the smaller FFN workloads (configs 1-3)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="read the rocprofv3 counter_collection.csv files of two --pmc-pass "
                          "runs (FETCH_SIZE, WRITE_SIZE), write profiles/hbm_traffic.json, exit")
@@ -362,8 +365,13 @@ def main() -> int:
         out["block_workload"] = measure_block(max(2, args.steps // 4), 1)
     if not args.no_ring:
         out["context_parallel_ring"] = measure_ring(max(2, args.steps // 4), 1)
+    cfg_outputs = None
+    if not args.no_configs:
+        out["configs"], cfg_outputs = measure_configs(max(4, args.steps), 2)
     if not args.no_cpu_baseline:
         out.update(cpu_baseline(host, w, Y, A, args.cpu_rows))
+        if cfg_outputs:
+            cpu_check_configs(out["configs"], cfg_outputs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -669,6 +677,121 @@ def measure_ring(steps: int, warmup: int) -> dict:
             "ring_tflops": round(fl / (ring_us * 1e-6) / 1e12, 1),
             "whole_tflops": round(fl / (full_us * 1e-6) / 1e12, 1),
             "max_err_vs_whole": diff}
+
+
+def measure_configs(steps: int, warmup: int):
+    """The smaller FFN workloads (tiny fp32 GELU, GPT-2-medium GELU, Llama-3-8B SwiGLU): all
+    ranks' tp_ffn_shard_fwd and the partial sum, per step, timed as a replayed graph (and
+    eagerly, with per-shard event times, for comparison).  Returns the results and, for the oracle check of the CPU-baseline
+    leg, the host inputs and the reduced outputs."""
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from megatron_tensor_transformer_gemm_amd import tpshard as S
+
+    res, keep = {}, {}
+    for cid in (1, 2, 3):
+        w = I.WORKLOADS[cid]
+        f32 = w.dtype == I.F32
+        code = S.TP_F32 if f32 else S.TP_BF16
+        tdt = torch.float32 if f32 else torch.bfloat16
+        gated = w.act == "swiglu"
+        names = ("x", "w1", "w3", "w2") if gated else ("x", "w1", "w2")
+        host = {k: I.make_tensor(w, k) for k in names}
+
+        def dev(a):
+            if f32:
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        X, W1, W2 = dev(host["x"]), dev(host["w1"]), dev(host["w2"])
+        W3 = dev(host["w3"]) if gated else None
+        T, d, d_ff, T_p = w.T, w.d, w.d_ff, w.T_p
+        n = d_ff // T_p
+        parts = torch.empty((T_p, T, d), dtype=tdt, device="cuda")
+        nb = S.tp_ffn_workspace_bytes(T, d_ff, T_p, code)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        y = torch.empty((T, d), dtype=tdt, device="cuda")
+
+        def step(evs=None):
+            for t in range(T_p):
+                if evs:
+                    evs[t][0].record()
+                S.tp_ffn_shard_fwd(X, W1, W3, W2, parts[t], ws, nb, T, d, d_ff, T_p, t, w.act, code, code)
+                if evs:
+                    evs[t][1].record()
+            S.tp_partial_sum(parts, T * d, T_p, None, y, T * d, code, code)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(T_p)]
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            step(ev[s_])
+        torch.cuda.synchronize()
+        ms_eager = (time.perf_counter() - t0) * 1e3 / steps
+        shard_us = 1e3 * sum(e[0].elapsed_time(e[1]) for es in ev for e in es) / (steps * T_p)
+        # Small problems finish before the host submits the next launch: replaying the step
+        # as one captured graph times the GPU's work alone.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(warmup):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        fl_shard = 2.0 * T * d * n * (2 if gated else 1) + 2.0 * T * n * d
+        peak = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
+        tf = T_p * fl_shard / (ms * 1e-3) / 1e12
+        res[w.name] = {"act": w.act, "dtype": "f32" if f32 else "bf16", "T": T, "d": d, "d_ff": d_ff,
+                       "T_p": T_p, "ms_per_step": round(ms, 4), "timing": "graph replay",
+                       "step_tflops": round(tf, 2), "step_frac_peak": round(tf / peak, 4),
+                       "peak_tflops": peak, "eager_ms_per_step": round(ms_eager, 4),
+                       "eager_shard_fwd_us": round(shard_us, 2)}
+        keep[w.name] = (w, host, y)
+        log(f"[bench] {w.name}: {ms:.3f} ms/step as a graph ({tf:.1f} TFLOP/s, all ranks + sum); "
+            f"eager {ms_eager:.3f} ms")
+    return res, keep
+
+
+def cpu_check_configs(results: dict, kept: dict, rows_n: int = 64) -> None:
+    """The oracle on a seeded sample of token rows of each smaller workload, against the
+    GPU's reduced output y (normwise max error, and the oracle's time for the sample)."""
+    import numpy as np
+
+    from megatron_tensor_transformer_gemm_amd import inputs as I
+    from oracle import tp_oracle as O
+
+    for name, (w, host, y) in kept.items():
+        g = np.random.default_rng(4321 + w.cid)
+        rows = np.unique(np.concatenate([[0, w.T - 1], g.choice(w.T, size=min(rows_n, w.T), replace=False)]))
+        x = I.as_f64(host["x"], w.dtype)[rows]
+        w1, w2 = I.as_f64(host["w1"], w.dtype), I.as_f64(host["w2"], w.dtype)
+        w3 = I.as_f64(host["w3"], w.dtype) if "w3" in host else None
+        t0 = time.perf_counter()
+        ref = O.partial_sum([O.ffn_shard(x, w1, w3, w2, w.T_p, t, w.act)[1] for t in range(w.T_p)])
+        secs = time.perf_counter() - t0
+        got = y.float().cpu().numpy().astype(np.float64)[rows]
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        tol = 1e-5 if w.dtype == I.F32 else 2e-2
+        results[name].update({"max_err": err, "tolerance": tol, "pass": err <= tol,
+                              "oracle_rows": int(len(rows)), "oracle_seconds": round(secs, 2)})
+        if err > tol:
+            log(f"[bench] PARITY FAILURE: {name} max_err {err:.3e} > {tol}")
 
 
 def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
