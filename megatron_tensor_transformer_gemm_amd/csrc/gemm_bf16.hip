@@ -531,8 +531,12 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     for (int i = 0; i + 1 < g.nseg; ++i) half += (g.Nx[i] + 127) / 128;
     const int64_t t256 = ((g.M + 255) / 256) * half;
     if (t256 >= 128) {
-      // When 192-row tiles also fit in one wave, the wave is the same and each tile does 3/4
-      // of the work (the GPT block's fused QKV, 2048 x 3x768: 144 -> 198 tiles, 86 -> 72 us)
+      // The smallest tile that still fits in one wave: the wave is the same and each tile
+      // does less work.  128x128 (GPT-2-medium's 4096 x 1024 products: 128 -> 256 tiles,
+      // 27 -> 22 us with GELU), else 192x128 (the GPT block's fused QKV, 2048 x 3x768:
+      // 144 -> 198 tiles, 86 -> 72 us).
+      if (t256 <= 256 && ((g.M + 127) / 128) * half <= 256)
+        return launch_cfg<128, 128, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
       if (t256 <= 256 && ((g.M + 191) / 192) * half <= 256) {
         if (kdepth > 2048) return launch_cfg<192, 128, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
         return launch_cfg<192, 128, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
