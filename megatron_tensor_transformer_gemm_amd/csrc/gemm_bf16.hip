@@ -65,23 +65,53 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
   tn = in / gm;
 }
 
-__device__ __forceinline__ float gelu_erf(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+// Activation arithmetic on the hardware's exp2 and reciprocal (each within about 1 ulp),
+// far below the bf16 rounding of the outputs.
+constexpr float kLog2e = 1.4426950408889634f;
+// logistic s(u) = 1 / (1 + e^-u)
+__device__ __forceinline__ float logistic(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
 }
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+__device__ __forceinline__ float silu(float u) { return u * logistic(u); }
+// erfc(x) by the Chebyshev-fitted form of Press et al., "Numerical Recipes" (erfcc):
+// t = 1 / (1 + |x|/2), erfc(|x|) = t exp(-x^2 + P(t)) with a degree-9 polynomial P,
+// fractional error below 1.2e-7 for every x; erfc(-|x|) = 2 - erfc(|x|).  Evaluating
+// Phi(u) = erfc(-u / sqrt 2) / 2 this way keeps the relative accuracy of GELU's
+// negative tail, which 1 + erf(u / sqrt 2) loses to cancellation.
+__device__ __forceinline__ float erfc_cheb(float x) {
+  const float z = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.5f * z);
+  float p = 0.17087277f;
+  p = __builtin_fmaf(p, t, -0.82215223f);
+  p = __builtin_fmaf(p, t, 1.48851587f);
+  p = __builtin_fmaf(p, t, -1.13520398f);
+  p = __builtin_fmaf(p, t, 0.27886807f);
+  p = __builtin_fmaf(p, t, -0.18628806f);
+  p = __builtin_fmaf(p, t, 0.09678418f);
+  p = __builtin_fmaf(p, t, 0.37409196f);
+  p = __builtin_fmaf(p, t, 1.00002368f);
+  p = __builtin_fmaf(p, t, -1.26551223f);
+  const float r = t * __builtin_amdgcn_exp2f((p - z * z) * kLog2e);
+  return x >= 0.0f ? r : 2.0f - r;
+}
+// standard normal distribution function Phi(u)
+__device__ __forceinline__ float norm_cdf(float u) {
+  return 0.5f * erfc_cheb(-0.70710678118654752f * u);
+}
+__device__ __forceinline__ float gelu(float u) { return u * norm_cdf(u); }
 
 template <int ACT>
 __device__ __forceinline__ float epilogue(float u, float v) {
-  if constexpr (ACT == kActGelu) return gelu_erf(u);
+  if constexpr (ACT == kActGelu) return gelu(u);
   else if constexpr (ACT == kActSwiglu) return silu(u) * v;
   else if constexpr (ACT == kActBilinear) return u * v;
   else return u;
 }
 
 // dU (and dV) from dH and the pre-activations u, v: the chain rule through the activation.
+// gelu'(u) = Phi(u) + u phi(u), phi the standard normal density
 __device__ __forceinline__ float gelu_grad(float u) {
-  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) +
-         u * 0.39894228040143268f * expf(-0.5f * u * u);
+  return norm_cdf(u) + u * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.5f * kLog2e * u * u);
 }
 template <int ACT>
 __device__ __forceinline__ void act_backward(float dh, float u, float v, float& du, float& dv) {
@@ -89,7 +119,7 @@ __device__ __forceinline__ void act_backward(float dh, float u, float v, float& 
     du = dh * gelu_grad(u);
     dv = 0.0f;
   } else if constexpr (ACT == kActSwiglu) {
-    const float sg = 1.0f / (1.0f + expf(-u));
+    const float sg = logistic(u);
     du = dh * v * sg * (1.0f + u * (1.0f - sg));
     dv = dh * u * sg;
   } else if constexpr (ACT == kActBilinear) {
