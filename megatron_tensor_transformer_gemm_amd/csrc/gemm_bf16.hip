@@ -457,6 +457,44 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // the trailing zero-fill copies must land before this workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // ---- epilogue without an activation, bf16 out, 256-wide tiles: through LDS.  Each lane
+  // holds 4 consecutive columns of 16 rows per accumulator block, so direct stores write
+  // 16 bytes into each of 32 rows per instruction.  Instead every wave rounds its 128 x 128
+  // block into a free stage buffer (rows of 256 B, 16-byte chunk c of row r at c ^ (r mod
+  // 16): conflict-free both ways) and stores it back row by row, 4 whole 256-byte row
+  // segments per instruction (row GEMM 1,003 -> 966 us, out-projection 377 -> 334 us).
+  constexpr int SREG = WTM * WCOLS * 2;   // one wave's block, bf16
+  if constexpr (ACT == kActNone && !DUAL && !OUT_F32 && !SAVE && WCOLS == 128 && STAGE % SREG == 0) {
+    if ((N_ & 7) == 0) {
+      __syncthreads();   // every wave's copies have landed and its fragment reads are done
+      const int off = wave * SREG;
+      LDS_AS unsigned char* R = buf(off / STAGE) + off % STAGE;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 32 + (lane & 31);
+#pragma unroll
+        for (int nb = 0; nb < NBS; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = nb * 32 + 8 * q + 4 * (lane >> 5);
+            const f32x16& a = acc[mb][nb];
+            *(LDS_AS bf16x4*)(R + r * 256 + ((((c >> 3) ^ r) & 15) << 4) + (c & 7) * 2) =
+                bf16x4{(__bf16)a[4 * q], (__bf16)a[4 * q + 1], (__bf16)a[4 * q + 2], (__bf16)a[4 * q + 3]};
+          }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < WTM / 4; ++it) {
+        const int row = 4 * it + (lane >> 4), ch = lane & 15;
+        const int r = wm * WTM + row;
+        const int n = n0 + wn * WCOLS + ch * 8;
+        const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * 256 + (((ch ^ row) & 15) << 4));
+        if (r < rows_left && n < N_) *(bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n) = v;
+      }
+      return;
+    }
+  }
+
   // ---- epilogue: activation on the fp32 accumulators, one rounding, vector stores
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
