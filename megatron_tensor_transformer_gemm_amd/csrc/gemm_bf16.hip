@@ -457,15 +457,23 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // the trailing zero-fill copies must land before this workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue without an activation, bf16 out, 256-wide tiles: through LDS.  Each lane
-  // holds 4 consecutive columns of 16 rows per accumulator block, so direct stores write
-  // 16 bytes into each of 32 rows per instruction.  Instead every wave rounds its 128 x 128
-  // block into a free stage buffer (rows of 256 B, 16-byte chunk c of row r at c ^ (r mod
-  // 16): conflict-free both ways) and stores it back row by row, 4 whole 256-byte row
-  // segments per instruction (row GEMM 1,003 -> 966 us, out-projection 377 -> 334 us).
+  // ---- bf16 outputs through LDS.  Each lane holds 4 consecutive columns of 16 rows per
+  // accumulator block, so direct stores write 8 bytes into each of 32 rows per
+  // instruction.  Instead every wave rounds its WTM x WCOLS block (the forward activation
+  // applied first) into a free stage buffer, rows of WCOLS*2 bytes with 16-byte chunk c of
+  // row r at c ^ (r mod chunks-per-row), and stores it back as whole row segments: 256 or
+  // 128 bytes per row, 4 or 8 rows per instruction (row GEMM 1,003 -> 966 us,
+  // out-projection 377 -> 334 us).  The training forward's extra U/V outputs, the
+  // derivative epilogues and fp32 outputs keep the direct stores below.
   constexpr int SREG = WTM * WCOLS * 2;   // one wave's block, bf16
-  if constexpr (ACT == kActNone && !DUAL && !OUT_F32 && !SAVE && WCOLS == 128 && STAGE % SREG == 0) {
+  constexpr bool STAGED = !OUT_F32 && !SAVE && (WCOLS == 64 || WCOLS == 128) &&
+                          (ACT == kActNone || LAYOUT == kNN) && STAGE % SREG == 0 &&
+                          4 * SREG <= NST * STAGE;
+  if constexpr (STAGED) {
     if ((N_ & 7) == 0) {
+      constexpr int SCH = WCOLS / 8;        // 16-byte chunks per staged row
+      constexpr int SPITCH = WCOLS * 2;     // bytes per staged row
+      constexpr int SRPI = 64 / SCH;        // rows per store instruction
       __syncthreads();   // every wave's copies have landed and its fragment reads are done
       const int off = wave * SREG;
       LDS_AS unsigned char* R = buf(off / STAGE) + off % STAGE;
@@ -477,18 +485,24 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = nb * 32 + 8 * q + 4 * (lane >> 5);
-            const f32x16& a = acc[mb][nb];
-            *(LDS_AS bf16x4*)(R + r * 256 + ((((c >> 3) ^ r) & 15) << 4) + (c & 7) * 2) =
-                bf16x4{(__bf16)a[4 * q], (__bf16)a[4 * q + 1], (__bf16)a[4 * q + 2], (__bf16)a[4 * q + 3]};
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = acc[mb][nb][4 * q + e];
+              if constexpr (LAYOUT == kNN) v[e] = epilogue<ACT>(u, DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f);
+              else v[e] = u;
+            }
+            *(LDS_AS bf16x4*)(R + r * SPITCH + ((((c >> 3) ^ r) & (SCH - 1)) << 4) + (c & 7) * 2) =
+                bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           }
       }
       __syncthreads();
 #pragma unroll 4
-      for (int it = 0; it < WTM / 4; ++it) {
-        const int row = 4 * it + (lane >> 4), ch = lane & 15;
+      for (int it = 0; it < WTM / SRPI; ++it) {
+        const int row = SRPI * it + lane / SCH, ch = lane % SCH;
         const int r = wm * WTM + row;
         const int n = n0 + wn * WCOLS + ch * 8;
-        const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * 256 + (((ch ^ row) & 15) << 4));
+        const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (((ch ^ row) & (SCH - 1)) << 4));
         if (r < rows_left && n < N_) *(bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n) = v;
       }
       return;
