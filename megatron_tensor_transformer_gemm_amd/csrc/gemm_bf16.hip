@@ -15,8 +15,8 @@
 //    out-of-range rows/columns/k come back as zeros from the buffer
 //    descriptor's range check (masked lanes get an out-of-range offset), so
 //    ragged M, N and K need no separate edge code.
-//  * Two LDS stages (double buffering): tile k+1 streams in while tile k is
-//    multiplied.
+//  * Two to four LDS stages in flight: later k-tiles stream in while the current
+//    one is multiplied.
 //  * A fragments: ds_read_b128 of 8 consecutive k of one row.
 //  * B fragments: B is N-contiguous in memory and in LDS; ds_read_b64_tr_b16
 //    transposes 4 k-rows x 16 columns per 16-lane group on the way to the
