@@ -57,10 +57,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str, per_launch_units: float):
+def load_traffic(kernel: str, workload: str, path: str | None = None):
     """HBM traffic of the dominant kernel from the committed PMC summary, if it still
     describes the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -307,7 +307,7 @@ def main() -> int:
     col_tf = tfl(fl_col, avg_us["col"])
     roofline = {"bound": "mfma", "achieved": round(col_tf, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(col_tf / PEAK_BF16_TFLOPS, 4),
-                "traffic": load_traffic("column_gemm_swiglu", w.name, fl_col),
+                "traffic": load_traffic("column_gemm_swiglu", w.name),
                 "kernel": "column-parallel GEMM + SwiGLU epilogue (per rank)",
                 "flops_per_launch": fl_col}
     if sclk:
@@ -381,7 +381,7 @@ def main() -> int:
 PMC_PASS_KERNELS = ["column_gemm_swiglu", "row_gemm", "partial_sum", "attn_outproj_gemm"]
 
 
-def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
+def ingest_pmc(fetch_csv: str, write_csv: str, out_path: str | None = None) -> int:
     """Per-launch HBM bytes of each kernel of the --pmc-pass run.
 
     FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by
@@ -412,7 +412,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
         out["kernels"][f"{name}@llama3_70b_swiglu_bf16"] = {
             "kernel_symbol": fetch[i][0], "fetch_bytes": fb, "write_bytes": wb,
             "bytes_per_launch": fb + wb, "source_digest": out["source_digest"]}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out["kernels"], indent=1))

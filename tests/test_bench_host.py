@@ -1,0 +1,73 @@
+"""Host-side bookkeeping of bench.py: the refusal of several GPUs, the HBM-counter
+ingestion (per-dispatch counters scaled by a plain copy of known size) and the rule that
+the committed traffic figure is used only while the GEMM sources are unchanged."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def _counter_csv(path, counter, rows):
+    """rows: (dispatch id, kernel name, KiB), written in the given order."""
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
+        wr.writeheader()
+        for did, name, kib in rows:
+            wr.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter,
+                         "Counter_Value": kib})
+
+
+def test_ingest_scales_by_the_copy_and_keeps_dispatch_order(tmp_path):
+    # dispatch order of --pmc-pass: the four kernels, a fill, then the 1 GiB copy.  The copy
+    # is read as half its bytes by the fetch counter and exactly by the write counter, so
+    # the fetched figures must come out doubled and the written ones unchanged.
+    names = ["gemm_col", "gemm_row", "psum", "gemm_out", "fill", "__amd_rocclr_copyBuffer"]
+    fetch_kib = [1000.0, 2000.0, 3000.0, 4000.0, 5.0, float(1 << 19)]
+    write_kib = [10.0, 20.0, 30.0, 40.0, 5.0, float(1 << 20)]
+    ids = range(1, len(names) + 1)
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the fetch file lists its dispatches last to first: the ingestion orders them by id
+    _counter_csv(f, "FETCH_SIZE", list(zip(ids, names, fetch_kib))[::-1])
+    _counter_csv(w, "WRITE_SIZE", list(zip(ids, names, write_kib)))
+    out = tmp_path / "traffic.json"
+    assert bench.ingest_pmc(str(f), str(w), str(out)) == 0
+    rec = json.load(open(out))
+    assert rec["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_scale"] == pytest.approx(1.0)
+    for i, key in enumerate(bench.PMC_PASS_KERNELS):
+        ent = rec["kernels"][f"{key}@llama3_70b_swiglu_bf16"]
+        assert ent["kernel_symbol"] == names[i]
+        assert ent["fetch_bytes"] == pytest.approx(fetch_kib[i] * 1024 * 2)
+        assert ent["write_bytes"] == pytest.approx(write_kib[i] * 1024)
+        assert ent["bytes_per_launch"] == pytest.approx(ent["fetch_bytes"] + ent["write_bytes"])
+        assert ent["source_digest"] == bench.kernel_source_digest()
+
+
+def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path):
+    path = tmp_path / "traffic.json"
+    key = "column_gemm_swiglu@llama3_70b_swiglu_bf16"
+    rec = {"kernels": {key: {"bytes_per_launch": 123.0,
+                             "source_digest": bench.kernel_source_digest()}}}
+    path.write_text(json.dumps(rec))
+    assert bench.load_traffic("column_gemm_swiglu", "llama3_70b_swiglu_bf16", str(path)) == 123.0
+    rec["kernels"][key]["source_digest"] = "0" * 16
+    path.write_text(json.dumps(rec))
+    assert bench.load_traffic("column_gemm_swiglu", "llama3_70b_swiglu_bf16", str(path)) is None
+    assert bench.load_traffic("row_gemm", "llama3_70b_swiglu_bf16", str(path)) is None
+    assert bench.load_traffic("column_gemm_swiglu", "x", str(tmp_path / "missing.json")) is None
