@@ -184,7 +184,13 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // the XOR swizzles of m/n-contiguous tiles mask the chunk index: those widths are powers
   // of two (k-contiguous A tiles may have any multiple of 64 rows, e.g. 192)
   static_assert(A_KC || (BM & (BM - 1)) == 0, "m-contiguous A tile width");
-  static_assert(B_KC || (BNS & (BNS - 1)) == 0, "n-contiguous B tile width");
+  // n-contiguous B rows of a power-of-two chunk count take the full swizzle; other widths
+  // (192 columns: 24 chunks) XOR only the low 3 bits, which keeps every chunk inside its
+  // aligned group of 8 and so stays a permutation of the row's chunks
+  constexpr int BSWM = (CPR & (CPR - 1)) == 0 ? CPR - 1 : 7;
+  static_assert(B_KC || (CPR & (CPR - 1)) == 0 || CPR % 8 == 0, "n-contiguous B tile width");
+  static_assert(A_BYTES % 4096 == 0 && (NSUB * SUB_BYTES) % 4096 == 0,
+                "copies split evenly over the 4 waves");
   static_assert(BM % 64 == 0, "two waves of 32-row blocks per tile column");
   static_assert(KSUB % 2 == 0 && (ACPR == 4 || ACPR == 8), "BK must be 32 or 64");
   static_assert(NST >= 2 && NST <= 5 && (NST - 1) * LPS <= 63, "stages");
@@ -280,7 +286,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       b_kr[i] = 8 * c;
     } else {
       const int row = pos / CPR;
-      const int c = (pos % CPR) ^ (swz_b(row) & (CPR - 1));
+      const int c = (pos % CPR) ^ (swz_b(row) & BSWM);
       b_voff[i] = (n0 + 8 * c < N_) ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
       b_kr[i] = row;
     }
@@ -339,7 +345,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       a_rd[mb] = (uint32_t)(krow_l * MPITCH + (((n >> 3) ^ swm) << 4) + ((n >> 2) & 1) * 8);
     }
   }
-  const int sw = swz_b(krow_l) & (CPR - 1);
+  const int sw = swz_b(krow_l) & BSWM;
   const int bcol = wn * WCOLS + (lane & 31);
   uint32_t b_rd[B_KC ? KSUB : NB];
   if constexpr (B_KC) {
@@ -602,6 +608,19 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     }
   }
   if constexpr (LAYOUT == kNN && !DUAL) {
+    // Below one full wave of 256x256 tiles, 128x192 tiles can fill the CUs where 256- and
+    // 128-wide ones leave a quarter idle: the GPT block's 2048 x 3072 column GEMM + GELU
+    // runs 256 of them instead of 192 tiles of 256x128 (115 -> 104 us).  256x192 tiles for
+    // its 2048 x 6144 products (256 instead of 192 tiles of 256x256) measured level for
+    // the row GEMM and 9 % slower for the out-projection: their 96-column wave blocks
+    // lose the LDS-staged bf16 epilogue.
+    if (g.nseg == 1 && big < 256 && g.N % 192 == 0) {
+      const int64_t t128 = ((g.M + 127) / 128) * (g.N / 192);
+      if (t128 >= 224 && t128 <= 256) {
+        if (kdepth > 2048) return launch_cfg<128, 192, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+        return launch_cfg<128, 192, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      }
+    }
     // Forward products of a few thousand tokens (measured at 2048 x 2304..6144 x 768..6144):
     // 256x256 tiles already pay off when they occupy 3/4 of the CUs, else 256x128 tiles
     // when those occupy half of them; 128x128 only below that.

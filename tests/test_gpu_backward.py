@@ -92,12 +92,15 @@ def test_backward_integer_bit_exact(act, shape):
 
 # ----------------------------------------------------------------------------- training forward
 @pytest.mark.parametrize("act", ["gelu", "swiglu", "bilinear"])
-def test_train_forward_keeps_preactivations(act):
+@pytest.mark.parametrize("shape", [(520, 264, 1056, 4, 2), (2000, 2048, 6144, 2, 1)],
+                         ids=["small", "192-col-tiles"])
+def test_train_forward_keeps_preactivations(act, shape):
     """y and H equal the plain forward bit for bit; U (V) equal the column product with no
-    activation bit for bit (same kernels, same accumulation), and the oracle within tolerance."""
-    T, d, d_ff, T_p, t = 520, 264, 1056, 4, 2
+    activation bit for bit (same kernels, same accumulation), and the oracle within tolerance.
+    The second shape's ungated column products run as 256 tiles of 128 x 192."""
+    T, d, d_ff, T_p, t = shape
     n = d_ff // T_p
-    log(f"[train-fwd] act={act}")
+    log(f"[train-fwd] act={act} shape={shape}")
     c = I.small_ffn_case(11, T, d, d_ff, act, I.BF16)
     xd, w1d, w2d = dev(c["x"], I.BF16), dev(c["w1"], I.BF16), dev(c["w2"], I.BF16)
     w3d = dev(c["w3"], I.BF16) if act in GATED else None

@@ -33,8 +33,9 @@ def _run_shard(xd, w1d, w3d, w2d, T, d, d_ff, T_p, t, act, in_code, out_code, y=
 
 # ----------------------------------------------------------------------------- bit-exact offsets
 @pytest.mark.parametrize("act", ["none", "bilinear"])
-@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (8200, 2056, 2, 1032), (2000, 264, 1, 2304)],
-                         ids=["small-tiles", "large-tiles", "192-row-tiles"])
+@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (8200, 2056, 2, 1032), (2000, 264, 1, 2304),
+                                   (2000, 5376, 2, 3072)],
+                         ids=["small-tiles", "large-tiles", "192-row-tiles", "192-col-tiles"])
 def test_integer_offsets_bit_exact(act, shape):
     """Integer inputs: H(t) and y(t) (fp32 out) must equal the oracle bit for bit."""
     T, d, T_p, n = shape
@@ -61,6 +62,8 @@ CASES = [
     (513, 1032, 4112, 2, "swiglu", I.BF16, I.BF16),
     (3000, 2048, 8192, 4, "gelu", I.BF16, I.BF16),
     (2000, 1032, 2304, 1, "gelu", I.BF16, I.BF16),     # 198 tiles of 192 x 128
+    (2000, 5376, 6144, 2, "gelu", I.BF16, I.BF16),     # 256 tiles of 128 x 192 (32-k)
+    (2000, 2048, 6144, 2, "gelu", I.BF16, I.F32),      # 256 tiles of 128 x 192 (64-k)
     (1, 64, 64, 1, "gelu", I.BF16, I.BF16),
 ]
 
