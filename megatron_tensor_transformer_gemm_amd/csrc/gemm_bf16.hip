@@ -184,11 +184,16 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // the XOR swizzles of m/n-contiguous tiles mask the chunk index: those widths are powers
   // of two (k-contiguous A tiles may have any multiple of 64 rows, e.g. 192)
   static_assert(A_KC || (BM & (BM - 1)) == 0, "m-contiguous A tile width");
-  // n-contiguous B rows of a power-of-two chunk count take the full swizzle; other widths
-  // (192 columns: 24 chunks) XOR only the low 3 bits, which keeps every chunk inside its
-  // aligned group of 8 and so stays a permutation of the row's chunks
-  constexpr int BSWM = (CPR & (CPR - 1)) == 0 ? CPR - 1 : 7;
-  static_assert(B_KC || (CPR & (CPR - 1)) == 0 || CPR % 8 == 0, "n-contiguous B tile width");
+  // Swizzle of n-contiguous B rows.  Power-of-two chunk counts take swz_b.  Rows of 24
+  // chunks (192 columns, 384 bytes) put k-rows r and r+2 on the same banks; XOR by
+  // 2 (r mod 4) gives the four k-rows of a transposing read disjoint 32-byte pairs and
+  // 64-byte quads, and touches only the low 3 bits, so every chunk stays inside its
+  // aligned group of 8 (a permutation of the row's chunks).
+  static_assert(B_KC || (CPR & (CPR - 1)) == 0 || CPR == 24, "n-contiguous B tile width");
+  auto swz_n = [](int r) -> int {
+    if constexpr ((CPR & (CPR - 1)) == 0) return swz_b(r) & (CPR - 1);
+    else return (r & 3) << 1;
+  };
   static_assert(A_BYTES % 4096 == 0 && (NSUB * SUB_BYTES) % 4096 == 0,
                 "copies split evenly over the 4 waves");
   static_assert(BM % 64 == 0, "two waves of 32-row blocks per tile column");
@@ -286,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       b_kr[i] = 8 * c;
     } else {
       const int row = pos / CPR;
-      const int c = (pos % CPR) ^ (swz_b(row) & BSWM);
+      const int c = (pos % CPR) ^ swz_n(row);
       b_voff[i] = (n0 + 8 * c < N_) ? (uint32_t)(row * ldb_ + 8 * c) * 2u : kOOB;
       b_kr[i] = row;
     }
@@ -345,7 +350,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       a_rd[mb] = (uint32_t)(krow_l * MPITCH + (((n >> 3) ^ swm) << 4) + ((n >> 2) & 1) * 8);
     }
   }
-  const int sw = swz_b(krow_l) & BSWM;
+  const int sw = swz_n(krow_l);
   const int bcol = wn * WCOLS + (lane & 31);
   uint32_t b_rd[B_KC ? KSUB : NB];
   if constexpr (B_KC) {
