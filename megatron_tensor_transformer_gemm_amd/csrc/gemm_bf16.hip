@@ -476,18 +476,32 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // 128 bytes per row, 4 or 8 rows per instruction (row GEMM 1,003 -> 966 us,
   // out-projection 377 -> 334 us).  The training forward's extra U/V outputs, the
   // derivative epilogues and fp32 outputs keep the direct stores below.
+  // 96-column wave blocks (192-column tiles) stage too: their rows of 12 chunks swizzle
+  // within aligned groups of 4, each wave's region lies inside one stage buffer, and the
+  // stores walk the block's chunks in order, 64 per instruction, across row boundaries.
   constexpr int SREG = WTM * WCOLS * 2;   // one wave's block, bf16
-  constexpr bool STAGED = !OUT_F32 && !SAVE && (WCOLS == 64 || WCOLS == 128) &&
-                          (ACT == kActNone || LAYOUT == kNN) && STAGE % SREG == 0 &&
-                          4 * SREG <= NST * STAGE;
+  constexpr bool POW2W = WCOLS == 64 || WCOLS == 128;
+  constexpr int SPB = STAGE / SREG;       // wave regions per stage buffer (96-column blocks)
+  constexpr bool STAGED = !OUT_F32 && !SAVE && (ACT == kActNone || LAYOUT == kNN) &&
+                          (POW2W ? STAGE % SREG == 0 && 4 * SREG <= NST * STAGE
+                                 : WCOLS == 96 && SPB >= 1 && 4 <= NST * SPB);
   if constexpr (STAGED) {
     if ((N_ & 7) == 0) {
       constexpr int SCH = WCOLS / 8;        // 16-byte chunks per staged row
       constexpr int SPITCH = WCOLS * 2;     // bytes per staged row
-      constexpr int SRPI = 64 / SCH;        // rows per store instruction
+      // physical chunk of chunk c in staged row r
+      auto spos = [](int r, int c) -> int {
+        if constexpr (POW2W) return (c ^ r) & (SCH - 1);
+        else return (c & ~3) | ((c ^ r) & 3);
+      };
       __syncthreads();   // every wave's copies have landed and its fragment reads are done
-      const int off = wave * SREG;
-      LDS_AS unsigned char* R = buf(off / STAGE) + off % STAGE;
+      LDS_AS unsigned char* R;
+      if constexpr (POW2W) {
+        const int off = wave * SREG;
+        R = buf(off / STAGE) + off % STAGE;
+      } else {
+        R = buf(wave / SPB) + (wave % SPB) * SREG;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int r = mb * 32 + (lane & 31);
@@ -503,18 +517,32 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
               if constexpr (LAYOUT == kNN) v[e] = epilogue<ACT>(u, DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f);
               else v[e] = u;
             }
-            *(LDS_AS bf16x4*)(R + r * SPITCH + ((((c >> 3) ^ r) & (SCH - 1)) << 4) + (c & 7) * 2) =
+            *(LDS_AS bf16x4*)(R + r * SPITCH + (spos(r, c >> 3) << 4) + (c & 7) * 2) =
                 bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           }
       }
       __syncthreads();
+      if constexpr (POW2W) {
+        constexpr int SRPI = 64 / SCH;      // rows per store instruction
 #pragma unroll 4
-      for (int it = 0; it < WTM / SRPI; ++it) {
-        const int row = SRPI * it + lane / SCH, ch = lane % SCH;
-        const int r = wm * WTM + row;
-        const int n = n0 + wn * WCOLS + ch * 8;
-        const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (((ch ^ row) & (SCH - 1)) << 4));
-        if (r < rows_left && n < N_) *(bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n) = v;
+        for (int it = 0; it < WTM / SRPI; ++it) {
+          const int row = SRPI * it + lane / SCH, ch = lane % SCH;
+          const int r = wm * WTM + row;
+          const int n = n0 + wn * WCOLS + ch * 8;
+          const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
+          if (r < rows_left && n < N_) *(bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n) = v;
+        }
+      } else {
+        static_assert((WTM * SCH) % 64 == 0, "whole store instructions");
+#pragma unroll 4
+        for (int it = 0; it < WTM * SCH / 64; ++it) {
+          const int idx = it * 64 + lane;
+          const int row = idx / SCH, ch = idx % SCH;
+          const int r = wm * WTM + row;
+          const int n = n0 + wn * WCOLS + ch * 8;
+          const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
+          if (r < rows_left && n < N_) *(bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n) = v;
+        }
       }
       return;
     }
@@ -613,14 +641,18 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     }
   }
   if constexpr (LAYOUT == kNN && !DUAL) {
-    // Below one full wave of 256x256 tiles, 128x192 tiles can fill the CUs where 256- and
-    // 128-wide ones leave a quarter idle: the GPT block's 2048 x 3072 column GEMM + GELU
-    // runs 256 of them instead of 192 tiles of 256x128 (115 -> 104 us).  256x192 tiles for
-    // its 2048 x 6144 products (256 instead of 192 tiles of 256x256) measured level for
-    // the row GEMM and 9 % slower for the out-projection: their 96-column wave blocks
-    // lose the LDS-staged bf16 epilogue.
+    // Below one full wave of 256x256 tiles, 192-column tiles can fill the CUs where 256- and
+    // 128-column ones leave a quarter idle.  The GPT block's 2048 x 6144 products take 256
+    // tiles of 256x192 instead of 192 of 256x256 (row GEMM 81.9 -> 76.5 us, out-projection
+    // 30.9 -> 28.7 us); its 2048 x 3072 column GEMM + GELU 256 tiles of 128x192 instead of
+    // 192 of 256x128 (115 -> 102 us).
     if (g.nseg == 1 && big < 256 && g.N % 192 == 0) {
-      const int64_t t128 = ((g.M + 127) / 128) * (g.N / 192);
+      const int64_t c192 = g.N / 192;
+      const int64_t t256 = ((g.M + 255) / 256) * c192, t128 = ((g.M + 127) / 128) * c192;
+      if (t256 >= 224 && t256 <= 256) {
+        if (kdepth > 2048) return launch_cfg<256, 192, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+        return launch_cfg<256, 192, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      }
       if (t128 >= 224 && t128 <= 256) {
         if (kdepth > 2048) return launch_cfg<128, 192, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
         return launch_cfg<128, 192, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);

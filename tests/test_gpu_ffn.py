@@ -62,8 +62,12 @@ CASES = [
     (513, 1032, 4112, 2, "swiglu", I.BF16, I.BF16),
     (3000, 2048, 8192, 4, "gelu", I.BF16, I.BF16),
     (2000, 1032, 2304, 1, "gelu", I.BF16, I.BF16),     # 198 tiles of 192 x 128
-    (2000, 5376, 6144, 2, "gelu", I.BF16, I.BF16),     # 256 tiles of 128 x 192 (32-k)
-    (2000, 2048, 6144, 2, "gelu", I.BF16, I.F32),      # 256 tiles of 128 x 192 (64-k)
+    # sub-wave products on 192-column tiles: column 128 x 192 (32-k), row 256 x 192 (32-k,
+    # ragged last tile row); column 128 x 192 (64-k); row 256 x 192 (64-k, bf16 and fp32 out)
+    (2000, 5376, 6144, 2, "gelu", I.BF16, I.BF16),
+    (2000, 2048, 6144, 2, "gelu", I.BF16, I.F32),
+    (2048, 6144, 1536, 2, "gelu", I.BF16, I.BF16),
+    (2048, 6144, 1536, 2, "gelu", I.BF16, I.F32),
     (1, 64, 64, 1, "gelu", I.BF16, I.BF16),
 ]
 
