@@ -476,9 +476,12 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // 128 bytes per row, 4 or 8 rows per instruction (row GEMM 1,003 -> 966 us,
   // out-projection 377 -> 334 us).  The training forward's extra U/V outputs, the
   // derivative epilogues and fp32 outputs keep the direct stores below.
-  // 96-column wave blocks (192-column tiles) stage too: their rows of 12 chunks swizzle
-  // within aligned groups of 4, each wave's region lies inside one stage buffer, and the
-  // stores walk the block's chunks in order, 64 per instruction, across row boundaries.
+  // 96-column wave blocks (192-column tiles) stage too: each wave's region lies inside one
+  // stage buffer, and the stores walk the block's chunks in order, 64 per instruction,
+  // across row boundaries.  Their 192-byte rows repeat the bank pattern every 4 rows, so
+  // chunks are permuted within aligned groups of 4 by r / 4: the 32 rows an 8-byte staging
+  // write touches fall 2 to a bank group (the floor for half a wave of 8-byte writes),
+  // against 8 with r mod 4; the 16-byte row-segment reads stay conflict-free.
   constexpr int SREG = WTM * WCOLS * 2;   // one wave's block, bf16
   constexpr bool POW2W = WCOLS == 64 || WCOLS == 128;
   constexpr int SPB = STAGE / SREG;       // wave regions per stage buffer (96-column blocks)
@@ -492,7 +495,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       // physical chunk of chunk c in staged row r
       auto spos = [](int r, int c) -> int {
         if constexpr (POW2W) return (c ^ r) & (SCH - 1);
-        else return (c & ~3) | ((c ^ r) & 3);
+        else return (c & ~3) | ((c ^ (r >> 2)) & 3);
       };
       __syncthreads();   // every wave's copies have landed and its fragment reads are done
       LDS_AS unsigned char* R;
