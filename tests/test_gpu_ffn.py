@@ -103,6 +103,36 @@ def test_ffn_shard_parity_small(case):
     assert e <= tol
 
 
+# ----------------------------------------------------------------------------- largest extents
+def _extent_case(T, d, d_ff, T_p, act, seed):
+    log(f"[extent] T={T} d={d} d_ff={d_ff} T_p={T_p} act={act}")
+    c = I.small_ffn_case(seed, T, d, d_ff, act, I.BF16)
+    gated = act == "swiglu"
+    xd, w1d, w2d = dev(c["x"], I.BF16), dev(c["w1"], I.BF16), dev(c["w2"], I.BF16)
+    w3d = dev(c["w3"], I.BF16) if gated else None
+    x, w1, w2 = f64(c["x"], I.BF16), f64(c["w1"], I.BF16), f64(c["w2"], I.BF16)
+    w3 = f64(c["w3"], I.BF16) if gated else None
+    for t in range(T_p):
+        y, h = _run_shard(xd, w1d, w3d, w2d, T, d, d_ff, T_p, t, act, S.TP_BF16, S.TP_BF16)
+        h_ref, y_ref = O.ffn_shard(x, w1, w3, w2, T_p, t, act)
+        eh, ey = nerr(host64(h), h_ref), nerr(host64(y), y_ref)
+        log(f"   t={t} err(H)={eh:.3e} err(y)={ey:.3e}")
+        assert eh <= BF16_TOL and ey <= BF16_TOL
+
+
+def test_largest_feature_extent():
+    """d = 2^20, the largest feature extent the library accepts (one more multiple of 8 is
+    rejected): a 256-row activation tile then spans 512 MB of per-lane byte offsets, the
+    column GEMM runs a 2^20-deep k-loop and the row GEMM 4,096 tiles of y(t)."""
+    _extent_case(24, 1 << 20, 64, 1, "gelu", 41)
+
+
+def test_largest_hidden_extent():
+    """d_ff = 2^20 with SwiGLU over 2 ranks: each rank's W1/W3 column blocks start 2^19
+    columns apart in rows of 2^20 elements, and its row GEMM runs a 2^19-deep k-loop."""
+    _extent_case(40, 64, 1 << 20, 2, "swiglu", 42)
+
+
 def _workload_tensors(w):
     names = ["x", "w1", "w2"] + (["w3"] if w.act == "swiglu" else [])
     return {k: I.make_tensor(w, k) for k in names}
