@@ -140,6 +140,8 @@ def main() -> int:
                     help="skip the extra measurement of the FFN shard backward")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the extra measurement of ring attention (context parallelism)")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-library reference (torch.matmul) on the same products")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the extra measurement of the smaller FFN workloads (configs 1-3)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -359,6 +361,9 @@ def main() -> int:
         "rows_equal_full_sum": out_rs_equal}
     log(f"[bench] reduce-scatter: 8 ranks {rs_us:.1f} us (full sum {avg_us['psum']:.1f} us)")
 
+    if not args.no_vendor:
+        out["vendor_reference"] = measure_vendor(S, w, X, W1, W3, W2, H, O_t[0], WO, P[0],
+                                                 max(4, args.steps // 2))
     if not args.no_backward:
         out["backward"] = measure_backward(w, X, W1, W3, W2, max(2, args.steps // 4), 1)
     if not args.no_block:
@@ -417,6 +422,64 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out_path: str | None = None) -> i
         json.dump(out, f, indent=1)
     print(json.dumps(out["kernels"], indent=1))
     return 0
+
+
+def measure_vendor(S, w, X, W1, W3, W2, H, O0, WO, Y0, steps) -> dict:
+    """The vendor library beside this library on rank 0's products of the 70B step, both
+    timed the same way: one product repeated on the same operands, events on the current
+    stream, after the step's timed region.  The library is torch.matmul (hipBLASLt on
+    ROCm) on the same bf16 operands and layouts (weight blocks as strided slices of the
+    full matrices); it runs the column product as two plain products X W1(0), X W3(0)
+    without the activation.  Repeating one product keeps its operands in the 256 MB MALL,
+    so these times are shorter than inside the step, where every rank reads its own
+    blocks."""
+    import torch
+
+    T, d, d_ff, T_p = w.T, w.d, w.d_ff, w.T_p
+    n, kdim = d_ff // T_p, (w.n_heads // T_p) * w.head_dim
+    BF = S.TP_BF16
+    U = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(U)
+    W1b, W3b, W2b, WOb = W1[:, :n], W3[:, :n], W2[:n, :], WO[:kdim, :]
+    prods = {
+        "column_gemm_swiglu": (
+            lambda: S.tp_ffn_column_fwd(X, W1, W3, H, T, d, d_ff, T_p, 0, S.TP_ACT_SWIGLU, BF),
+            lambda: (torch.matmul(X, W1b, out=U), torch.matmul(X, W3b, out=V)),
+            2 * 2.0 * T * d * n),
+        "row_gemm": (
+            lambda: S.tp_ffn_row_fwd(H, W2, Y0, T, d, d_ff, T_p, 0, BF, BF),
+            lambda: torch.matmul(H, W2b, out=Y0), 2.0 * T * n * d),
+        "attn_outproj_gemm": (
+            lambda: S.tp_attn_outproj_shard_fwd(O0, WO, Y0, T, d, w.n_heads, w.n_kv_heads,
+                                                w.head_dim, T_p, 0, BF, BF),
+            lambda: torch.matmul(O0, WOb, out=Y0), 2.0 * T * kdim * d),
+    }
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    res = {"library": "torch.matmul (hipBLASLt), same operands; its column product is two "
+                      "plain products without the activation",
+           "timing": "one product repeated on the same operands (MALL-resident), both sides"}
+    for name, (ours, vendor, fl) in prods.items():
+        t_o, t_v = timed(ours), timed(vendor)
+        t_o2 = timed(ours)   # again, so that neither side always runs on the colder chip
+        t_o = min(t_o, t_o2)
+        res[name] = {"ours_us": round(t_o, 1), "ours_tflops": round(fl / t_o / 1e6, 1),
+                     "vendor_us": round(t_v, 1), "vendor_tflops": round(fl / t_v / 1e6, 1),
+                     "ours_over_vendor_time": round(t_o / t_v, 3)}
+        log(f"[bench] {name}, repeated: ours {t_o:.1f} us, vendor {t_v:.1f} us")
+    return res
 
 
 def measure_backward(w, X, W1, W3, W2, steps: int, warmup: int) -> dict:
