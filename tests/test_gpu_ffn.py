@@ -68,6 +68,8 @@ CASES = [
     (2000, 2048, 6144, 2, "gelu", I.BF16, I.F32),
     (2048, 6144, 1536, 2, "gelu", I.BF16, I.BF16),
     (2048, 6144, 1536, 2, "gelu", I.BF16, I.F32),
+    # row GEMM of 33 x 33 256 x 256 tiles, ragged in both M and N
+    (8200, 8200, 512, 2, "gelu", I.BF16, I.BF16),
     (1, 64, 64, 1, "gelu", I.BF16, I.BF16),
 ]
 
