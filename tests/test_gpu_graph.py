@@ -37,11 +37,16 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-def test_forward_step_graph_replays_match_eager():
-    T, d, d_ff, T_p, act = 1000, 328, 1600, 2, "swiglu"
+@pytest.mark.parametrize("case", [(1000, 328, 1600, 2, "swiglu"), (2000, 5376, 6144, 2, "gelu")],
+                         ids=["swiglu-small", "gelu-192-column-tiles"])
+def test_forward_step_graph_replays_match_eager(case):
+    """The second case runs the column GEMM on 128 x 192 tiles and the row GEMM on 256 x 192
+    tiles, both with the LDS-staged bf16 epilogue."""
+    T, d, d_ff, T_p, act = case
     log(f"[graph] forward step T={T} d={d} d_ff={d_ff} T_p={T_p} {act}")
     c = I.small_ffn_case(41, T, d, d_ff, act, I.BF16)
-    x, w1, w3, w2 = (dev(c[k], I.BF16) for k in ("x", "w1", "w3", "w2"))
+    x, w1, w2 = (dev(c[k], I.BF16) for k in ("x", "w1", "w2"))
+    w3 = dev(c["w3"], I.BF16) if "w3" in c else None
     res = dev(I.bf16_bits(np.random.default_rng(3).standard_normal((T, d)).astype(np.float32)), I.BF16)
     parts = torch.empty((T_p, T, d), dtype=torch.bfloat16, device="cuda:0")
     nb = S.tp_ffn_workspace_bytes(T, d_ff, T_p, BF)
