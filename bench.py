@@ -72,6 +72,45 @@ def load_traffic(kernel: str, workload: str, path: str | None = None):
     return ent.get("bytes_per_launch")
 
 
+def host_cpu_info() -> dict:
+    """The host's CPU model, its physical cores and the logical CPUs this process may use
+    (from /proc/cpuinfo and the affinity mask)."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "usable_logical_cpus": usable}
+
+
+def percentiles(vals) -> dict:
+    """Median, p10 and p90 of a list of durations (nearest-rank)."""
+    v = sorted(vals)
+
+    def at(q):
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": at(0.5), "p10": at(0.1), "p90": at(0.9), "calls": len(v)}
+
+
 class SclkSampler:
     """Samples the shader clock from a host thread while the GPU works: the current DPM
     level (the line marked '*') of the card's pp_dpm_sclk, every `period_s` seconds.
@@ -361,6 +400,7 @@ def main() -> int:
         "rows_equal_full_sum": out_rs_equal}
     log(f"[bench] reduce-scatter: 8 ranks {rs_us:.1f} us (full sum {avg_us['psum']:.1f} us)")
 
+    out["shard_fwd_calls"] = measure_shard_calls(S, w, X, W1, W3, W2, H, P, 50)
     if not args.no_vendor:
         out["vendor_reference"] = measure_vendor(S, w, X, W1, W3, W2, H, O_t[0], WO, P[0],
                                                  max(4, args.steps // 2))
@@ -372,7 +412,7 @@ def main() -> int:
         out["context_parallel_ring"] = measure_ring(max(2, args.steps // 4), 1)
     cfg_outputs = None
     if not args.no_configs:
-        out["configs"], cfg_outputs = measure_configs(max(4, args.steps), 2)
+        out["configs"], cfg_outputs = measure_configs(max(8, args.steps), 2)
     if not args.no_cpu_baseline:
         out.update(cpu_baseline(host, w, Y, A, args.cpu_rows))
         if cfg_outputs:
@@ -380,7 +420,65 @@ def main() -> int:
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    failures = parity_failures(out)
+    if failures:
+        log("[bench] PARITY FAILURE in: " + ", ".join(failures))
+        return 3
     return 0
+
+
+def parity_failures(out: dict) -> list:
+    """Names of the checks in the result that did not meet their tolerance."""
+    bad = []
+    if out.get("max_err") and not out["max_err"].get("pass", False):
+        bad.append("max_err")
+    for name, r in (out.get("configs") or {}).items():
+        if "pass" in r and not r["pass"]:
+            bad.append(f"configs.{name}")
+    ring = out.get("context_parallel_ring")
+    if ring and not ring["max_err_vs_whole"] <= TOL:
+        bad.append("context_parallel_ring")
+    sp = out.get("sequence_parallel")
+    if sp and not sp["rows_equal_full_sum"]:
+        bad.append("sequence_parallel")
+    return bad
+
+
+def measure_shard_calls(S, w, X, W1, W3, W2, H, P, calls: int) -> dict:
+    """Per-call duration of tp_ffn_shard_fwd (column GEMM + SwiGLU, row GEMM) at the
+    headline shape: `calls` calls cycling over the ranks, each between its own pair of HIP
+    events on the launch stream; median and p10/p90."""
+    import torch
+
+    T, d, d_ff, T_p = w.T, w.d, w.d_ff, w.T_p
+    n = d_ff // T_p
+    BF = S.TP_BF16
+    nb = S.tp_ffn_workspace_bytes(T, d_ff, T_p, BF)
+    ws = H.view(torch.uint8).view(-1)
+    assert ws.numel() >= nb
+    for t in range(2):
+        S.tp_ffn_shard_fwd(X, W1, W3, W2, P[t], ws, nb, T, d, d_ff, T_p, t, "swiglu", BF, BF)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    torch.cuda.synchronize()
+    for i in range(calls):
+        t = i % T_p
+        ev[i][0].record()
+        S.tp_ffn_shard_fwd(X, W1, W3, W2, P[t], ws, nb, T, d, d_ff, T_p, t, "swiglu", BF, BF)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = [1e3 * a.elapsed_time(b) for a, b in ev]
+    st = percentiles(us)
+    fl = 2.0 * T * d * n * 2 + 2.0 * T * n * d
+    res = {"what": f"{w.name}: tp_ffn_shard_fwd, one rank's whole FFN shard per call",
+           "median_us": round(st["median"], 1), "p10_us": round(st["p10"], 1),
+           "p90_us": round(st["p90"], 1), "calls": st["calls"],
+           "median_tflops": round(fl / (st["median"] * 1e-6) / 1e12, 1),
+           "median_frac_peak": round(fl / (st["median"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "flops_per_call": fl}
+    log(f"[bench] shard fwd calls: median {st['median']:.1f} us (p10 {st['p10']:.1f}, "
+        f"p90 {st['p90']:.1f}), {res['median_tflops']} TFLOP/s")
+    return res
 
 
 PMC_PASS_KERNELS = ["column_gemm_swiglu", "row_gemm", "partial_sum", "attn_outproj_gemm"]
@@ -795,7 +893,9 @@ def measure_configs(steps: int, warmup: int):
             step(ev[s_])
         torch.cuda.synchronize()
         ms_eager = (time.perf_counter() - t0) * 1e3 / steps
-        shard_us = 1e3 * sum(e[0].elapsed_time(e[1]) for es in ev for e in es) / (steps * T_p)
+        shard_calls = [1e3 * e[0].elapsed_time(e[1]) for es in ev for e in es]
+        shard_us = sum(shard_calls) / len(shard_calls)
+        shard_st = percentiles(shard_calls)
         # Small problems finish before the host submits the next launch: replaying the step
         # as one captured graph times the GPU's work alone.
         side = torch.cuda.Stream()
@@ -824,7 +924,11 @@ def measure_configs(steps: int, warmup: int):
                        "T_p": T_p, "ms_per_step": round(ms, 4), "timing": "graph replay",
                        "step_tflops": round(tf, 2), "step_frac_peak": round(tf / peak, 4),
                        "peak_tflops": peak, "eager_ms_per_step": round(ms_eager, 4),
-                       "eager_shard_fwd_us": round(shard_us, 2)}
+                       "eager_shard_fwd_us": round(shard_us, 2),
+                       "eager_shard_fwd_median_us": round(shard_st["median"], 2),
+                       "eager_shard_fwd_p10_us": round(shard_st["p10"], 2),
+                       "eager_shard_fwd_p90_us": round(shard_st["p90"], 2),
+                       "eager_shard_fwd_calls": shard_st["calls"]}
         keep[w.name] = (w, host, y)
         log(f"[bench] {w.name}: {ms:.3f} ms/step as a graph ({tf:.1f} TFLOP/s, all ranks + sum); "
             f"eager {ms_eager:.3f} ms")
@@ -857,9 +961,9 @@ def cpu_check_configs(results: dict, kept: dict, rows_n: int = 64) -> None:
             log(f"[bench] PARITY FAILURE: {name} max_err {err:.3e} > {tol}")
 
 
-def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
-    """Time the float64 oracle on a sample of token rows (all ranks, both sublayers) and
-    compare the GPU's reduced outputs at those rows."""
+def cpu_baseline(host, w, Y, A, rows_n: int, repeats: int = 3) -> dict:
+    """Time the float64 oracle on a sample of token rows (all ranks, both sublayers; median
+    of `repeats` passes) and compare the GPU's reduced outputs at those rows."""
     import numpy as np
 
     from megatron_tensor_transformer_gemm_amd import inputs as I
@@ -881,16 +985,23 @@ def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
     xs = I.as_f64(host["x"][rows], w.dtype)
     os_ = I.as_f64(host["o"][rows], w.dtype)
     w1, w3, w2, wo = (I.bf16_to_f32(host[k]) for k in ("w1", "w3", "w2", "wo"))
-    t0 = time.perf_counter()
-    y_parts, a_parts = [], []
-    for t in range(T_p):
-        _, y_t = O.ffn_shard(xs, w1, w3, w2, T_p, t, w.act)
-        y_parts.append(y_t)
-        a_parts.append(O.attn_outproj_shard(os_[:, t * kdim:(t + 1) * kdim], wo, w.n_heads,
-                                            w.n_kv_heads, w.head_dim, T_p, t))
-    y_ref = O.partial_sum(y_parts)
-    a_ref = O.partial_sum(a_parts)
-    cpu_s = time.perf_counter() - t0
+
+    def oracle_pass():
+        y_parts, a_parts = [], []
+        for t in range(T_p):
+            _, y_t = O.ffn_shard(xs, w1, w3, w2, T_p, t, w.act)
+            y_parts.append(y_t)
+            a_parts.append(O.attn_outproj_shard(os_[:, t * kdim:(t + 1) * kdim], wo, w.n_heads,
+                                                w.n_kv_heads, w.head_dim, T_p, t))
+        return O.partial_sum(y_parts), O.partial_sum(a_parts)
+
+    runs = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        y_ref, a_ref = oracle_pass()
+        runs.append(time.perf_counter() - t0)
+        log(f"[bench] oracle pass {len(runs)}/{repeats}: {runs[-1]:.1f} s")
+    cpu_s = sorted(runs)[len(runs) // 2]
     flops = T_p * R * (2.0 * d * n * 3 + 2.0 * kdim * d)
     yg = Y[rows].float().cpu().numpy()
     ag = A[rows].float().cpu().numpy()
@@ -902,6 +1013,10 @@ def cpu_baseline(host, w, Y, A, rows_n: int) -> dict:
     return {
         "cpu_baseline": {"value": round(flops / cpu_s / 1e12, 4), "unit": "TFLOP/s", "cores": cores,
                          "kind": "oracle", "seconds": round(cpu_s, 2),
+                         "timing": f"median of {len(runs)} passes",
+                         "pass_seconds": [round(r, 2) for r in runs],
+                         "cores_meaning": "BLAS threads the oracle's matrix products ran on",
+                         **host_cpu_info(),
                          "sample": f"{R} of {T} token rows (seeded, incl. first and last); all "
                                    f"{T_p} ranks' SwiGLU FFN shards and attention out-projection "
                                    f"shards plus both partial sums, float64 NumPy"},

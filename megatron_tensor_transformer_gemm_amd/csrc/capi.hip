@@ -387,9 +387,9 @@ int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t, int64_
   if (T_p < 1 || t < 0 || t >= T_p)
     return fail(TP_ERR_INVALID_ARG, "tp_attn_outproj_shard_fwd: rank t=%d outside [0, T_p=%d)", t, T_p);
   if (n_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d is not a multiple of T_p=%d", n_heads, T_p);
   if (n_kv_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_kv_heads=%d is not a multiple of T_p=%d", n_kv_heads, T_p);
   if (n_heads % n_kv_heads)
     return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
   if (!((in_dtype == TP_BF16 && (out_dtype == TP_BF16 || out_dtype == TP_F32)) ||
@@ -461,13 +461,13 @@ int attn_heads_impl(const char* fn, bool kvrep, const void* x, const void* wq, c
   if (T_p < 1 || t < 0 || t >= T_p)
     return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
   if (n_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d is not a multiple of T_p=%d", n_heads, T_p);
   const bool replicate = kvrep && n_kv_heads % T_p != 0;
   if (replicate && T_p % n_kv_heads)
     return fail(TP_ERR_NOT_DIVISIBLE, "TP%d cannot replicate %d KV heads evenly (T_p must be a multiple)",
                 T_p, n_kv_heads);
   if (!replicate && n_kv_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_kv_heads=%d is not a multiple of T_p=%d", n_kv_heads, T_p);
   if (n_heads % n_kv_heads)
     return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
   if (head_dim != 64 && head_dim != 128)
@@ -776,9 +776,9 @@ int tp_attn_outproj_shard_bwd(const void* o_t, const void* wo, const void* dy, v
   if (T_p < 1 || t < 0 || t >= T_p)
     return fail(TP_ERR_INVALID_ARG, "%s: rank t=%d outside [0, T_p=%d)", fn, t, T_p);
   if (n_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP degree %d must divide the query heads (%d)", T_p, n_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d is not a multiple of T_p=%d", n_heads, T_p);
   if (n_kv_heads % T_p)
-    return fail(TP_ERR_NOT_DIVISIBLE, "TP%d needs n_kv_heads divisible by %d, got %d", T_p, T_p, n_kv_heads);
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_kv_heads=%d is not a multiple of T_p=%d", n_kv_heads, T_p);
   if (n_heads % n_kv_heads)
     return fail(TP_ERR_INVALID_ARG, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads, n_kv_heads);
   if (grad_dtype != TP_BF16 && grad_dtype != TP_F32)

@@ -239,3 +239,44 @@ def integer_backward_case(T: int, d: int, d_ff: int, seed: int = 7) -> dict:
     dy = g.integers(-4, 5, size=(T, d)).astype(np.float32)
     return {"x": bf16_bits(x), "w1": bf16_bits(w1), "w3": bf16_bits(w3), "w2": bf16_bits(w2),
             "dy": bf16_bits(dy)}
+
+
+def bf16_grid(lo_exp: int, hi_exp: int, limit: float) -> np.ndarray:
+    """Every bfloat16 value v with 2^lo_exp <= |v| < 2^(hi_exp+1) and |v| <= limit, both
+    signs, plus +0 and -0, as float32 (each exactly a bf16 value)."""
+    mags = []
+    for e in range(lo_exp, hi_exp + 1):
+        mags.append(np.float32(2.0 ** e) * (1.0 + np.arange(128, dtype=np.float32) / 128.0))
+    m = np.concatenate(mags).astype(np.float32)
+    m = m[m <= limit]
+    return np.concatenate([m, -m, np.array([0.0, -0.0], dtype=np.float32)])
+
+
+def activation_grid_case(T: int, n: int, T_p: int, seed: int = 3) -> dict:
+    """Inputs that put chosen pre-activations into the column product exactly.
+
+    d = 2n.  x[:, :n] holds every bfloat16 value in [-12, 12] with magnitude at least
+    2^-20 (and +-0), tiled over the T x n cells in a seeded random order; x[:, n:] holds
+    the gate values: 1.0 in a seeded half of the cells, other bf16 values in [-4, 4]
+    elsewhere.  Every rank's block of W1 is [I_n; 0] and of W3 is [0; I_n], so each
+    rank's U = X W1(t) and V = X W3(t) are exactly x[:, :n] and x[:, n:] (one non-zero
+    product per sum).  Every rank's row block of W2 is [I_n | 0], so y(t) = [H | 0] and,
+    in the backward, dH = dY W2(t)^T = dy[:, :n] exactly.  dy holds bf16 values in
+    [-4, 4] (1.0 in a seeded quarter of the cells).  Returned as bf16 bit patterns."""
+    g = np.random.Generator(np.random.PCG64(636363 + seed))
+    grid = bf16_grid(-20, 3, 12.0)
+    reps = -(-T * n // grid.size)
+    u = np.concatenate([g.permutation(grid) for _ in range(reps)])[: T * n].reshape(T, n)
+    small = bf16_grid(-20, 1, 4.0)
+    v = g.choice(small, size=(T, n)).astype(np.float32)
+    v[g.random((T, n)) < 0.5] = 1.0
+    dy = g.choice(small, size=(T, 2 * n)).astype(np.float32)
+    dy[g.random((T, 2 * n)) < 0.25] = 1.0
+    eye = np.eye(n, dtype=np.float32)
+    zero = np.zeros((n, n), dtype=np.float32)
+    w1 = np.tile(np.vstack([eye, zero]), (1, T_p))
+    w3 = np.tile(np.vstack([zero, eye]), (1, T_p))
+    w2 = np.tile(np.hstack([eye, zero]), (T_p, 1))
+    x = np.hstack([u, v]).astype(np.float32)
+    return {"x": bf16_bits(x), "w1": bf16_bits(w1), "w3": bf16_bits(w3), "w2": bf16_bits(w2),
+            "dy": bf16_bits(dy)}

@@ -48,9 +48,9 @@ def head_shard(n_heads: int, n_kv_heads: int, head_dim: int, T_p: int, t: int) -
     divide both the query-head and the KV-head counts.
     """
     if n_heads % T_p:
-        raise ValueError(f"TP degree {T_p} must divide query heads ({n_heads})")
+        raise ValueError(f"n_heads={n_heads} is not a multiple of T_p={T_p}")
     if n_kv_heads % T_p:
-        raise ValueError(f"TP{T_p} needs n_kv_heads divisible by {T_p}, got {n_kv_heads}")
+        raise ValueError(f"n_kv_heads={n_kv_heads} is not a multiple of T_p={T_p}")
     h_t = n_heads // T_p
     kv_t = n_kv_heads // T_p
     return {
@@ -75,7 +75,7 @@ def head_shard_kv_replicated(n_heads: int, n_kv_heads: int, head_dim: int, T_p: 
     if n_kv_heads % T_p == 0:
         return head_shard(n_heads, n_kv_heads, head_dim, T_p, t)
     if n_heads % T_p:
-        raise ValueError(f"TP degree {T_p} must divide query heads ({n_heads})")
+        raise ValueError(f"n_heads={n_heads} is not a multiple of T_p={T_p}")
     if T_p % n_kv_heads or n_heads % n_kv_heads:
         raise ValueError(f"TP{T_p} cannot replicate {n_kv_heads} KV heads evenly")
     if not (0 <= t < T_p):
@@ -380,7 +380,9 @@ def attn_heads_shard(x, wq, wk, wv, n_heads: int, n_kv_heads: int, head_dim: int
     kb, _ = hs["kv_cols"]
     group = hs["h_t"] // hs["kv_t"]
     outs = []
-    need = x if rows is None else x[: int(np.max(rows)) + 1]
+    # a causal query row i needs only the keys and values of rows <= i; without the mask
+    # every row sees the whole sequence
+    need = x if (rows is None or not causal) else x[: int(np.max(rows)) + 1]
     for j in range(hs["h_t"]):
         c0 = qb + j * head_dim
         kc = kb + (j // group) * head_dim

@@ -71,3 +71,25 @@ def test_traffic_is_used_only_for_the_sources_it_was_measured_on(tmp_path):
     assert bench.load_traffic("column_gemm_swiglu", "llama3_70b_swiglu_bf16", str(path)) is None
     assert bench.load_traffic("row_gemm", "llama3_70b_swiglu_bf16", str(path)) is None
     assert bench.load_traffic("column_gemm_swiglu", "x", str(tmp_path / "missing.json")) is None
+
+
+def test_parity_failures_name_every_failed_check():
+    """bench.py exits non-zero (after printing its line) when any comparison with the oracle,
+    or the ring/whole-sequence and reduce-scatter/full-sum checks, misses its bar."""
+    good = {"max_err": {"pass": True}, "configs": {"a": {"pass": True}, "b": {}},
+            "context_parallel_ring": {"max_err_vs_whole": 1e-4},
+            "sequence_parallel": {"rows_equal_full_sum": True}}
+    assert bench.parity_failures(good) == []
+    assert bench.parity_failures({"cpu_baseline": None}) == []
+    bad = json.loads(json.dumps(good))
+    bad["max_err"]["pass"] = False
+    bad["configs"]["a"]["pass"] = False
+    bad["context_parallel_ring"]["max_err_vs_whole"] = float("nan")
+    bad["sequence_parallel"]["rows_equal_full_sum"] = False
+    assert bench.parity_failures(bad) == ["max_err", "configs.a", "context_parallel_ring",
+                                          "sequence_parallel"]
+
+
+def test_percentiles_nearest_rank():
+    st = bench.percentiles([float(v) for v in range(100, 0, -1)])
+    assert (st["median"], st["p10"], st["p90"], st["calls"]) == (51.0, 11.0, 90.0, 100)

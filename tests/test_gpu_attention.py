@@ -108,7 +108,7 @@ def test_outproj_workload_sampled():
     o_full = I.make_tensor(w, "o")
     wo = I.make_tensor(w, "wo")
     wod = dev(wo, I.BF16)
-    rows = sample_rows(w.T, 254, seed=41)
+    rows = sample_rows(w.T, 1024, seed=41)
     parts = torch.empty((T_p, w.T, w.d), dtype=torch.bfloat16, device="cuda:0")
     refs = []
     for t in range(T_p):
@@ -156,7 +156,8 @@ def run_block_sequence(w, dv, x_s, T_p):
 def test_gpt_block_workload_sampled():
     """GPT-style d=6144 TP8 block: 4 micro-batches of one 2048-token sequence run back to
     back through every rank's attention and FFN shards with the two local reduces; the
-    oracle checks sampled token rows of the first and last micro-batch."""
+    oracle checks 1,024 seeded token rows (plus the first and last) of every micro-batch
+    (a causal row i needs only the keys and values of rows 0..i)."""
     w = I.WORKLOADS[5]
     log(f"[block] {w.name}: generating inputs")
     host = {k: I.make_tensor(w, k) for k in ("x", "wq", "wk", "wv", "wo", "w1", "w2")}
@@ -168,8 +169,8 @@ def test_gpt_block_workload_sampled():
     for s in range(w.n_seq):
         outs.append(run_block_sequence(w, dv, xd[s * L:(s + 1) * L], w.T_p))
     torch.cuda.synchronize()
-    for s in (0, w.n_seq - 1):
-        rows = sample_rows(L, 126, seed=50 + s)
+    for s in range(w.n_seq):
+        rows = sample_rows(L, 1024, seed=50 + s)
         x_s = f64(host["x"][s * L:(s + 1) * L], I.BF16)
         x1_ref, y_ref = O.block_sequence(x_s, W64, w.n_heads, w.n_kv_heads, w.head_dim, w.T_p,
                                          act="gelu", rows=rows)
@@ -253,3 +254,28 @@ def test_attention_heads_kv_replicated_parity(n_heads, n_kv, T_p, dh):
                                       dh, T_p, t, True)
             torch.cuda.synchronize()
             assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("L,h_t,causal", [(8192, 6, True), (8192, 2, False), (32768, 2, True)])
+def test_attention_core_long_sequence_sampled(L, h_t, causal):
+    """Long sequences through tp_attn_core_fwd (one sequence, heads of 128): 1,024 seeded
+    query rows plus the first and last of every head against the oracle ("7.9 Tensor and
+    pipeline parallelism", section 6 on long contexts); causal row i depends only on keys
+    0..i, so sampled rows are checked exactly as in the whole result."""
+    dh = 128
+    log(f"[attn-long] L={L} h_t={h_t} causal={causal}")
+    g = np.random.default_rng(L + h_t)
+    q, k, v = (I.bf16_bits(g.standard_normal((L, h_t * dh)).astype(np.float32)) for _ in range(3))
+    o = torch.full((L, h_t * dh), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_attn_core_fwd(dev(q, I.BF16), dev(k, I.BF16), dev(v, I.BF16), o, 1, L, h_t, h_t, dh,
+                       h_t * dh, h_t * dh, h_t * dh, causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(L, 1024, seed=L + 7)
+    og = host64(o)
+    q64, k64, v64 = (f64(a, I.BF16) for a in (q, k, v))
+    for j in range(h_t):
+        sl = slice(j * dh, (j + 1) * dh)
+        ref = O.attention_head(q64[:, sl], k64[:, sl], v64[:, sl], causal=causal, rows=rows)
+        e = nerr(og[rows, sl], ref)
+        log(f"   head {j}: err(O)={e:.3e} on {len(rows)} rows")
+        assert e <= BF16_TOL

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from _gpu_util import BF16_TOL, dev, f64, host64, log, nerr, requires_gpu
+from _gpu_util import BF16_TOL, dev, f64, host64, log, nerr, requires_gpu, sample_rows
 from megatron_tensor_transformer_gemm_amd import inputs as I
 from megatron_tensor_transformer_gemm_amd import tpshard as S
 from oracle import tp_oracle as O
@@ -162,3 +162,45 @@ def test_ring_order_of_chunks_does_not_matter():
         outs.append((host64(st.o), host64(st.lse)))
     for o, lse in outs[1:]:
         assert nerr(o, outs[0][0]) <= 1e-5 and np.max(np.abs(lse - outs[0][1])) <= 1e-5
+
+
+def test_ring_long_sequence_sampled():
+    """Context parallelism at 8,192 causal tokens, a rank's 6 heads of 128, 4 chunks of 2,048
+    (the benchmark's ring): every CP rank folds its chunks, and 1,024 seeded rows (plus the
+    first and last) of the assembled output are checked against the oracle's attention over
+    the whole sequence; the most loaded rank's running state, which folds all four chunks,
+    is checked against the oracle's ring steps on every row of one head."""
+    C, L, h_t, dh = 4, 8192, 6, 128
+    c, kd = L // C, h_t * dh
+    log(f"[ring-long] C={C} L={L} h_t={h_t}")
+    g = np.random.default_rng(8192)
+    q, k, v = (I.bf16_bits(g.standard_normal((L, kd)).astype(np.float32)) for _ in range(3))
+    qd, kd_, vd = (dev(a, I.BF16) for a in (q, k, v))
+    out = torch.full((L, kd), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    states = []
+    for r in range(C):
+        st = Ring(c, h_t, dh)
+        for s_ in range(C):
+            src = (r - s_) % C
+            st.step(qd[r * c:], kd_[src * c:], vd[src * c:], 1, c, h_t, kd, kd, r * c, src * c, True)
+        out[r * c:(r + 1) * c] = st.finish()
+        states.append(st)
+    torch.cuda.synchronize()
+    rows = sample_rows(L, 1024, seed=99)
+    og = host64(out)
+    q64, k64, v64 = (f64(a, I.BF16) for a in (q, k, v))
+    for j in range(h_t):
+        sl = slice(j * dh, (j + 1) * dh)
+        ref = O.attention_head(q64[:, sl], k64[:, sl], v64[:, sl], causal=True, rows=rows)
+        e = nerr(og[rows, sl], ref)
+        log(f"   head {j}: err(O)={e:.3e}")
+        assert e <= BF16_TOL
+    r, j = C - 1, 1
+    sl = slice(j * dh, (j + 1) * dh)
+    ro, rl = np.zeros((c, dh)), np.full(c, -np.inf)
+    for s_ in range(C):
+        src = (r - s_) % C
+        ro, rl = O.ring_attention_step(q64[r * c:(r + 1) * c, sl], k64[src * c:(src + 1) * c, sl],
+                                       v64[src * c:(src + 1) * c, sl], ro, rl, r * c, src * c, True)
+    assert nerr(host64(states[r].o)[:, sl], ro) <= BF16_TOL
+    assert np.max(np.abs(host64(states[r].lse)[:, j] - rl)) <= LSE_TOL

@@ -13,6 +13,7 @@ import pytest
 import test_oracle_backward as bpins
 import test_oracle_pins as pins
 import test_oracle_ring as rpins
+from oracle import analytic as A
 from oracle import tp_oracle as O
 
 
@@ -144,6 +145,23 @@ def _ring_masks_diagonal(q, k, v, o_state, lse_state, q_pos0, k_pos0, causal=Tru
     return _orig_ring(q, k, v, o_state, lse_state, q_pos0 - 1, k_pos0, causal)
 
 
+_orig_heads = O.attn_heads_shard
+
+
+def _heads_truncated_kv(x, wq, wk, wv, n_heads, n_kv_heads, head_dim, T_p, t, causal=True,
+                        rows=None, kv_replicate=False):
+    """Cuts the keys and values after the last requested row even without the causal mask."""
+    if rows is not None:
+        x = np.asarray(x)[: int(np.max(rows)) + 1]
+    return _orig_heads(x, wq, wk, wv, n_heads, n_kv_heads, head_dim, T_p, t, causal, rows,
+                       kv_replicate)
+
+
+def _interleaved_step_squared(stages, micro_batches, v):
+    """Divides by v twice."""
+    return A.bubble_fraction(stages, micro_batches) / (v * v)
+
+
 MUTATIONS = [
     ("silu", _wrong_silu_sign, [lambda: pins.test_silu_closed_forms_and_library(),
                                 lambda: pins.test_brute_force_tiny("swiglu", 2)]),
@@ -168,6 +186,7 @@ MUTATIONS = [
                                                     lambda: rpins.test_ring_step_brute_force_tiny()]),
     ("ring_attention_step", _ring_lse_max, [lambda: rpins.test_ring_zero_queries_closed_form(),
                                             lambda: rpins.test_ring_equals_full_attention(3, False)]),
+    ("attn_heads_shard", _heads_truncated_kv, [lambda: pins.test_heads_shard_rows_equal_the_full_result_rows(False)]),
     ("ring_attention_step", _ring_masks_diagonal, [lambda: rpins.test_ring_zero_queries_closed_form(),
                                                    lambda: rpins.test_ring_equals_full_attention(4, True)]),
 ]
@@ -180,3 +199,9 @@ def test_planted_mistake_is_caught(monkeypatch, name, wrong, checks):
     for check in checks:
         with pytest.raises((AssertionError, ValueError)):
             check()
+
+
+def test_planted_interleaved_bubble_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "bubble_interleaved_step", _interleaved_step_squared)
+    with pytest.raises(AssertionError):
+        pins.test_interleaved_bubble_forms_agree()

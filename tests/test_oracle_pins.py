@@ -217,6 +217,24 @@ def test_block_sharded_equals_unsharded_and_rows():
     np.testing.assert_allclose(y_r, y[rows], atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_heads_shard_rows_equal_the_full_result_rows(causal):
+    """Restricting the computed query rows changes nothing but which rows come back: a
+    causal row i still sees keys 0..i, and a row without the mask sees every key, so rows
+    taken from the start, the middle and the end equal those rows of the full O(t)."""
+    rng = np.random.default_rng(29)
+    T, d, dh, H = 9, 12, 4, 4
+    x = rng.standard_normal((T, d))
+    wq, wk, wv = (rng.standard_normal((d, H * dh)) / math.sqrt(d) for _ in range(3))
+    for T_p in (1, 2):
+        for t in range(T_p):
+            full = O.attn_heads_shard(x, wq, wk, wv, H, H, dh, T_p, t, causal=causal)
+            for rows in ([0, 3], [2, 5, 8], [4], [0]):
+                got = O.attn_heads_shard(x, wq, wk, wv, H, H, dh, T_p, t, causal=causal,
+                                         rows=np.array(rows))
+                np.testing.assert_allclose(got, full[rows], rtol=0, atol=1e-13)
+
+
 @pytest.mark.parametrize("n_heads,n_kv,T_p", [(16, 2, 4), (16, 2, 8), (8, 1, 8), (16, 4, 2)])
 def test_kv_replicated_shards_equal_full_gqa(n_heads, n_kv, T_p):
     """With T_p above the KV heads (each KV head replicated on T_p / n_kv ranks), the ranks'
@@ -256,7 +274,7 @@ def test_kv_replication_needs_an_even_multiple():
 def test_gqa_divisibility():
     with pytest.raises(ValueError, match="n_kv_heads"):
         O.head_shard(64, 8, 128, 16, 0)
-    with pytest.raises(ValueError, match="query heads"):
+    with pytest.raises(ValueError, match="n_heads="):
         O.head_shard(48, 48, 128, 5, 0)
     hs = O.head_shard(64, 8, 128, 8, 3)
     assert hs["q_cols"] == (3 * 1024, 4 * 1024) and hs["kv_cols"] == (384, 512)
@@ -308,6 +326,29 @@ def test_bubble_four_stages_eight_micro_batches():
     assert analytic.bubble_fraction(4, 8) == Fraction(3, 11)
     # the two normalisations describe the same idle time
     assert analytic.bubble_vs_useful(4, 8) * 8 == analytic.bubble_fraction(4, 8) * 11
+
+
+def test_interleaved_bubble_forms_agree():
+    """The two pages print the interleaved bubble in two normalisations: per whole step,
+    (1/v) (P-1)/(M+P-1) ("7.9 ...", section 3.4), and per useful work, (p-1)/(v m)
+    ("Parallelism II: model", "Pipeline parallelism", whose 18.8 % and 9.4 % pin the
+    latter through the printed-value table).  The step form is the useful form times the
+    share M/(M+P-1) of a plain schedule's slots that do useful work, i.e. times
+    1 - bubble_fraction; with v = 1 it is the plain bubble, 3/11 for 4 stages and 8
+    micro-batches, about 18 % for P = 8, M = 32 and about 47 % for P = 8, M = 8 (3.2)."""
+    for P in range(1, 10):
+        for M in range(1, 40):
+            for v in (1, 2, 3, 4, 8):
+                step = analytic.bubble_interleaved_step(P, M, v)
+                useful = analytic.bubble_interleaved_useful(P, M, v)
+                assert step == useful * (1 - analytic.bubble_fraction(P, M)), (P, M, v)
+                assert step <= analytic.bubble_fraction(P, M)
+    assert analytic.bubble_interleaved_step(4, 8, 1) == Fraction(3, 11)
+    assert abs(float(analytic.bubble_interleaved_step(8, 32, 1)) - 0.18) <= 0.005
+    assert abs(float(analytic.bubble_interleaved_step(8, 8, 1)) - 0.47) <= 0.005
+    # p5's printed interleaved values, carried over to the step form
+    assert analytic.bubble_interleaved_step(4, 8, 2) == Fraction(3, 22)
+    assert analytic.bubble_interleaved_step(4, 8, 4) == Fraction(3, 44)
 
 
 @pytest.mark.parametrize("T_p", [1, 2, 4, 8])
