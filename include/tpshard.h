@@ -121,6 +121,29 @@ int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* 
                      int32_t act, int32_t in_dtype, int32_t out_dtype, void* hip_stream);
 
 /*
+ * tp_ffn_shard_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, the same two kernels, bit-identical results.
+ * H(t) lives in a buffer the library itself holds on each GPU it runs on: a
+ * file-scope device array of TP_NOALLOC_SCRATCH_BYTES (128 MiB), kept until the
+ * process ends; its address is looked up once per device, on the first call with
+ * that device current.  The call itself allocates and frees nothing.
+ *
+ *   T * (d_ff/T_p) * sizeof(element of in_dtype), rounded up to 256 bytes, must
+ *   not exceed TP_NOALLOC_SCRATCH_BYTES (TP_ERR_WORKSPACE otherwise; y_t untouched).
+ *
+ * All calls on one GPU share that buffer, which keeps the last call's H(t): calls
+ * that overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  hip_stream must belong to the current device.
+ * Errors: as tp_ffn_shard_fwd.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int tp_ffn_shard_fwd_noalloc(const void* x, const void* w1, const void* w3, const void* w2,
+                             void* y_t, int64_t T, int64_t d, int64_t d_ff, int32_t T_p,
+                             int32_t t, int32_t act, int32_t in_dtype, int32_t out_dtype,
+                             void* hip_stream);
+
+/*
  * The two halves of tp_ffn_shard_fwd, for callers that schedule them
  * separately (e.g. to overlap the previous sublayer's exchange with the
  * column-parallel product, or to time each kernel).

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "tp_internal.h"
@@ -187,6 +188,57 @@ int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* 
   const bool bf = in_dtype == TP_BF16;
   TRY(launch_column(x, w1, w3, workspace, T, d, d_ff, T_p, t, act, bf, s));
   return launch_row(workspace, w2, y_t, T, d, d_ff, T_p, t, bf, out_dtype == TP_F32, s);
+}
+
+}  // extern "C"
+
+// H(t) of tp_ffn_shard_fwd_noalloc.  In host code `scratch` names a host-side stand-in:
+// kernels get the device address looked up for the current device, never the name.
+static __device__ __align__(256) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on its first use there.
+int scratch_address(void** out) {
+  int dev = -1;
+  TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TP_ERR_UNSUPPORTED, "device %d outside the %d the library keeps scratch for", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p || !aligned16(p)) return fail(TP_ERR_HIP, "scratch address %p is not usable", p);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_ffn_shard_fwd_noalloc(const void* x, const void* w1, const void* w3, const void* w2,
+                             void* y_t, int64_t T, int64_t d, int64_t d_ff, int32_t T_p, int32_t t,
+                             int32_t act, int32_t in_dtype, int32_t out_dtype, void* hip_stream) {
+  const char* fn = "tp_ffn_shard_fwd_noalloc";
+  TRY(check_ffn(fn, x, w1, w3, w2, nullptr, y_t, T, d, d_ff, T_p, t, act, in_dtype, out_dtype, true, true));
+  if (T == 0) return TP_OK;
+  const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
+  if (need > TP_NOALLOC_SCRATCH_BYTES)
+    return fail(TP_ERR_WORKSPACE, "%s: H(t) needs %zu bytes, above the %zu bytes of scratch held per GPU",
+                fn, need, (size_t)TP_NOALLOC_SCRATCH_BYTES);
+  void* h = nullptr;
+  TRY(scratch_address(&h));
+  hipStream_t s = (hipStream_t)hip_stream;
+  const bool bf = in_dtype == TP_BF16;
+  TRY(launch_column(x, w1, w3, h, T, d, d_ff, T_p, t, act, bf, s));
+  return launch_row(h, w2, y_t, T, d, d_ff, T_p, t, bf, out_dtype == TP_F32, s);
 }
 
 int tp_ffn_column_fwd(const void* x, const void* w1, const void* w3, void* h_t, int64_t T, int64_t d,

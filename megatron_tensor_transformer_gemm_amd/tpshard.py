@@ -21,6 +21,7 @@ TP_OK, TP_ERR_INVALID_ARG, TP_ERR_NOT_DIVISIBLE, TP_ERR_WORKSPACE, TP_ERR_UNSUPP
     0, -1, -2, -3, -4, -5
 TP_ACT_NONE, TP_ACT_GELU, TP_ACT_SWIGLU, TP_ACT_BILINEAR = 0, 1, 2, 3
 TP_F32, TP_BF16 = 0, 1
+TP_NOALLOC_SCRATCH_BYTES = 128 << 20
 ACT = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU, "bilinear": TP_ACT_BILINEAR}
 STATUS_NAMES = {0: "TP_OK", -1: "TP_ERR_INVALID_ARG", -2: "TP_ERR_NOT_DIVISIBLE",
                 -3: "TP_ERR_WORKSPACE", -4: "TP_ERR_UNSUPPORTED", -5: "TP_ERR_HIP"}
@@ -41,6 +42,8 @@ _SIGS = {
     "tp_ffn_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "tp_ffn_shard_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _i32,
                                 _i32, _i32, _i32, _vp]),
+    "tp_ffn_shard_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                        _i32, _i32, _vp]),
     "tp_ffn_column_fwd": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "tp_ffn_row_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "tp_attn_outproj_shard_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
@@ -151,6 +154,15 @@ def tp_ffn_shard_fwd(x, w1, w3, w2, y_t, workspace, workspace_bytes, T, d, d_ff,
     _check("tp_ffn_shard_fwd", lib().tp_ffn_shard_fwd(
         _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y_t), _ptr(workspace), workspace_bytes,
         T, d, d_ff, T_p, t, act, in_dtype, out_dtype, _stream(hip_stream)))
+
+
+def tp_ffn_shard_fwd_noalloc(x, w1, w3, w2, y_t, T, d, d_ff, T_p, t, act, in_dtype, out_dtype,
+                             hip_stream=None):
+    if isinstance(act, str):
+        act = ACT[act]
+    _check("tp_ffn_shard_fwd_noalloc", lib().tp_ffn_shard_fwd_noalloc(
+        _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y_t), T, d, d_ff, T_p, t, act, in_dtype,
+        out_dtype, _stream(hip_stream)))
 
 
 def tp_ffn_column_fwd(x, w1, w3, h_t, T, d, d_ff, T_p, t, act, in_dtype, hip_stream=None):

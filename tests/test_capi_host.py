@@ -22,7 +22,7 @@ def L():
 
 def test_library_exports_every_declared_function(L):
     names = S.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert S.tp_abi_version() == 3
@@ -312,3 +312,28 @@ def test_ring_finish_rejects_before_launch(kw, code):
     with pytest.raises(S.TPError) as e:
         S.tp_attn_ring_finish(**a)
     assert e.value.code == code, S.tp_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=16384, d_ff=28672 * 2, T_p=8), S.TP_ERR_WORKSPACE),    # H(t) of 224 MiB > 128 MiB
+    (dict(T=1 << 20, d_ff=512, T_p=4), S.TP_ERR_WORKSPACE),        # 256 MiB
+    (dict(d_ff=1000, T_p=3), S.TP_ERR_NOT_DIVISIBLE),
+    (dict(w3=P), S.TP_ERR_INVALID_ARG),                             # W3 with GELU
+    (dict(y_t=MIS), S.TP_ERR_INVALID_ARG),
+    (dict(in_dtype=S.TP_F32, out_dtype=S.TP_BF16), S.TP_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_before_launch(kw, code):
+    """The allocation-free FFN entry point checks its arguments, and that H(t) fits the
+    library's per-GPU scratch, before it touches the device."""
+    a = dict(x=P, w1=P, w3=None, w2=P, y_t=P, T=64, d=256, d_ff=1024, T_p=2, t=0, act="gelu",
+             in_dtype=S.TP_BF16, out_dtype=S.TP_BF16, hip_stream=0)
+    a.update(kw)
+    with pytest.raises(S.TPError) as e:
+        S.tp_ffn_shard_fwd_noalloc(**a)
+    assert e.value.code == code, S.tp_last_error()
+
+
+def test_noalloc_limit_fits_the_70b_shard():
+    """128 MiB of scratch holds H(t) of the Llama-3-70B-shaped rank (16,384 x 3,584 bf16)."""
+    assert S.tp_ffn_workspace_bytes(16384, 28672, 8, S.TP_BF16) <= S.TP_NOALLOC_SCRATCH_BYTES
+    assert S.TP_NOALLOC_SCRATCH_BYTES == 128 << 20
