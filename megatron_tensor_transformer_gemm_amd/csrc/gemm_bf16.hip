@@ -299,7 +299,8 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // B sub-tile a wave's copies land in is the same for all of its copies.
   const bool b_second = (wave * B_LD) / QSUB != 0;
 
-  auto issue = [&](int kt, LDS_AS unsigned char* base) {
+  // Copies [first, first + count) of stage kt's LPS per wave (A copies first, then B).
+  auto issue_range = [&](int kt, LDS_AS unsigned char* base, int first, int count) {
     int k0 = kt * BK;
     int Kc = g.K;
     const __bf16* Ab = A;
@@ -318,16 +319,19 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
     const uint32_t lds = (uint32_t)(uintptr_t)base;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
+      if (i < first || i >= first + count) continue;
       const uint32_t v = (full || k0 + a_kc[i] < Kc) ? a_voff[i] : kOOB;
       copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (wave * A_LD + i) * 1024));
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
+      if (A_LD + i < first || A_LD + i >= first + count) continue;
       const uint32_t v = (full || k0 + b_kr[i] < Kc) ? b_voff[i] : kOOB;
       copy16_to_lds(db, v,
                     __builtin_amdgcn_readfirstlane(lds + A_BYTES + (wave * B_LD + i) * 1024));
     }
   };
+  auto issue = [&](int kt, LDS_AS unsigned char* base) { issue_range(kt, base, 0, LPS); };
 
   // ---- per-lane LDS read offsets
   // k-contiguous tiles: row r of the fragment at lane r % 32, chunk 2*s + lane / 32.
@@ -453,11 +457,34 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
     // Past the end the copies are all out of range (zero fill, no memory traffic), so
     // every stage issues the same number of copies and the loop has no branches.
     sync_copies<(NST - 2) * LPS>();
-    issue(kt + NST, cur);
+    if constexpr (LAYOUT != kNN) {
+      issue(kt + NST, cur);
+      // (after the last stage this reads a stale buffer; the fragments are not used)
+      load_frags(nxt, 0, af[0], bfr[0]);
+      mfmas(af[1], bfr[1]);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     // (after the last stage this reads a stale buffer; the fragments are not used)
     load_frags(nxt, 0, af[0], bfr[0]);
-    mfmas(af[1], bfr[1]);
-    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // The forward's last substep: its MFMAs with stage kt+NST's copies spread between
+    // them.  A copy holds its wave at issue for tens of cycles; issued as one block after
+    // the barrier they idled the matrix pipe for about a quarter of the loop (counted with
+    // cycle counters around the block); one at a time they overlap the MFMA in flight.
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+      const int mb = i / NB, nb = i % NB;
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][nb], af[1][mb], acc[mb][nb], 0, 0, 0);
+      // copies [i*LPS/NMFMA, (i+1)*LPS/NMFMA) follow MFMA i
+      const int c0 = i * LPS / NMFMA, c1 = (i + 1) * LPS / NMFMA;
+      if (c1 > c0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_range(kt + NST, cur, c0, c1 - c0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
