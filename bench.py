@@ -315,6 +315,7 @@ def main() -> int:
         for i, nm in enumerate(names):
             dur.setdefault(nm, []).append(ev[s][i].elapsed_time(ev[s][i + 1]))
     avg_us = {k: 1e3 * sum(v) / len(v) for k, v in dur.items()}
+    step_ms_each = [round(ev[s][0].elapsed_time(ev[s][n_kernels]), 3) for s in range(args.steps)]
 
     fl_col = 2.0 * T * d * n * 2
     fl_row = 2.0 * T * n * d
@@ -370,6 +371,7 @@ def main() -> int:
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "step_gemm_flops": step_flops,
         "kernels": kernels,
+        "step_ms_each": step_ms_each,
         "roofline": roofline,
         "sclk": sclk,
     }

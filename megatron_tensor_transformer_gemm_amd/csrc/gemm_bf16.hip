@@ -407,6 +407,21 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       }
     }
   };
+  // Fragment read group j of substep s: j < MB an A fragment, else a B fragment (its two
+  // transposing reads); the forward's last substep interleaves them one group at a time.
+  auto read_group = [&](const LDS_AS unsigned char* As, int s, bf16x8 (&af)[MB], bf16x8 (&bfr)[NB],
+                        int j) {
+    const LDS_AS unsigned char* Bs = As + A_BYTES;
+    if (j < MB) {
+      af[j] = *(const LDS_AS bf16x8*)(As + a_rd[s] + j * 32 * AROWB);
+    } else {
+      const int nb = j - MB;
+      const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
+      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+      bfr[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
   auto mfmas = [&](const bf16x8 (&af)[MB], const bf16x8 (&bfr)[NB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -466,26 +481,28 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
-    // (after the last stage this reads a stale buffer; the fragments are not used)
-    load_frags(nxt, 0, af[0], bfr[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    // The forward's last substep: its MFMAs with stage kt+NST's copies spread between
-    // them.  A copy holds its wave at issue for tens of cycles; issued as one block after
-    // the barrier they idled the matrix pipe for about a quarter of the loop (counted with
-    // cycle counters around the block); one at a time they overlap the MFMA in flight.
+    // The forward's last substep: its MFMAs with stage kt+NST's copies and then the next
+    // stage's first fragment reads spread between them, items j = 0 .. LPS+NFR-1 (copies
+    // first) after MFMA j*NMFMA/(LPS+NFR).  A copy holds its wave at issue for tens of
+    // cycles: issued as one block after the barrier they idled the matrix pipe for about a
+    // quarter of the loop (cycle counters around the block); one at a time they overlap the
+    // MFMA in flight, and with no fragment reads in flight yet they stall less.
+    // (After the last stage the reads see a stale buffer; those fragments are not used.)
+    constexpr int NFR = MB + NB;
+    constexpr int NITEM = LPS + NFR;
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int mb = i / NB, nb = i % NB;
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][nb], af[1][mb], acc[mb][nb], 0, 0, 0);
-      // copies [i*LPS/NMFMA, (i+1)*LPS/NMFMA) follow MFMA i
-      const int c0 = i * LPS / NMFMA, c1 = (i + 1) * LPS / NMFMA;
-      if (c1 > c0) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue_range(kt + NST, cur, c0, c1 - c0);
-        __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NITEM; ++j) {
+        if (j * NMFMA / NITEM != i) continue;
+        if (j < LPS) issue_range(kt + NST, cur, j, 1);
+        else read_group(nxt, 0, af[0], bfr[0], j - LPS);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   for (int kt0 = 0; kt0 < nk; kt0 += NST) {
