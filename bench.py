@@ -690,13 +690,14 @@ def measure_block(steps: int, warmup: int) -> dict:
     o_t = torch.empty((L, kdim), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(S.tp_attn_heads_workspace_bytes(1, L, H, H, dh, T_p), dtype=torch.uint8,
                      device="cuda")
-    Hh = torch.empty((L, n), dtype=torch.bfloat16, device="cuda")
+    nbf = S.tp_ffn_workspace_bytes(L, w.d_ff, T_p, BF)   # H(t) and the split-K scratch
+    wsf = torch.empty(nbf, dtype=torch.uint8, device="cuda")
     x1 = torch.empty((L, d), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((w.T, d), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     names = []
     for _ in range(w.n_seq):
-        names += ["attn_heads", "outproj"] * T_p + ["psum"] + ["col", "row"] * T_p + ["psum"]
+        names += ["attn_heads", "outproj"] * T_p + ["psum"] + ["ffn"] * T_p + ["psum"]
 
     def step(evs=None):
         k = [0]
@@ -718,9 +719,8 @@ def measure_block(steps: int, warmup: int) -> dict:
             S.tp_partial_sum(Pf, stride, T_p, xs, x1, L * d, BF, BF)
             mark()
             for t in range(T_p):
-                S.tp_ffn_column_fwd(x1, Wd["w1"], None, Hh, L, d, w.d_ff, T_p, t, S.TP_ACT_GELU, BF)
-                mark()
-                S.tp_ffn_row_fwd(Hh, Wd["w2"], P[t], L, d, w.d_ff, T_p, t, BF, BF)
+                S.tp_ffn_shard_fwd(x1, Wd["w1"], None, Wd["w2"], P[t], wsf, nbf, L, d, w.d_ff, T_p, t,
+                                   S.TP_ACT_GELU, BF, BF)
                 mark()
             S.tp_partial_sum(Pf, stride, T_p, x1, y[s_ * L:(s_ + 1) * L], L * d, BF, BF)
             mark()
@@ -771,8 +771,9 @@ def measure_block(steps: int, warmup: int) -> dict:
             "attention_core_causal": {"avg_us": round(core_us, 2), "tflops": tf(fl_core, core_us),
                                       "frac_peak": round(fl_core / (core_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "attn_outproj_gemm": {"avg_us": round(avg["outproj"], 2), "tflops": tf(fl_out, avg["outproj"])},
-            "column_gemm_gelu": {"avg_us": round(avg["col"], 2), "tflops": tf(fl_ffn1, avg["col"])},
-            "row_gemm": {"avg_us": round(avg["row"], 2), "tflops": tf(fl_ffn2, avg["row"])},
+            "ffn_shard_gelu": {"avg_us": round(avg["ffn"], 2), "tflops": tf(fl_ffn1 + fl_ffn2, avg["ffn"]),
+                               "what": "tp_ffn_shard_fwd: column GEMM + GELU (split-K when it "
+                                       "cannot fill the GPU) and row GEMM"},
             "partial_sum_residual": {"avg_us": round(avg["psum"], 2)},
         },
     }

@@ -79,7 +79,14 @@ size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_d
   if (T < 0 || d_ff <= 0 || T_p < 1 || d_ff % T_p) return 0;
   if (in_dtype != TP_F32 && in_dtype != TP_BF16) return 0;
   const size_t elt = in_dtype == TP_BF16 ? 2 : 4;
-  return round256((size_t)T * (size_t)(d_ff / T_p) * elt);
+  const size_t h = round256((size_t)T * (size_t)(d_ff / T_p) * elt);
+  if (in_dtype != TP_BF16 || d_ff / T_p > kMaxExtent) return h;
+  // plus the column product's split-K scratch when it is too small to fill the GPU (its k
+  // depth d is not an argument: sized for a deep product, for either activation kind)
+  const int32_t n = (int32_t)(d_ff / T_p);
+  const size_t plain = tpk::splitk_scratch_bytes(T, 1, &n, int64_t(1) << 30, false);
+  const size_t gated = tpk::splitk_scratch_bytes(T, 1, &n, int64_t(1) << 30, true);
+  return h + round256(plain > gated ? plain : gated);
 }
 
 }  // extern "C"
@@ -124,7 +131,8 @@ int check_ffn(const char* fn, const void* x, const void* w1, const void* w3, con
 }
 
 int launch_column(const void* x, const void* w1, const void* w3, void* h, int64_t T, int64_t d,
-                  int64_t d_ff, int32_t T_p, int32_t t, int32_t act, bool bf, hipStream_t s) {
+                  int64_t d_ff, int32_t T_p, int32_t t, int32_t act, bool bf, hipStream_t s,
+                  void* part = nullptr, size_t part_bytes = 0) {
   const int64_t n = d_ff / T_p;
   const size_t elt = bf ? 2 : 4;
   const bool gated = act == TP_ACT_SWIGLU || act == TP_ACT_BILINEAR;
@@ -142,6 +150,10 @@ int launch_column(const void* x, const void* w1, const void* w3, void* h, int64_
   g.ldc = (int32_t)n;
   g.act = act;
   g.out_f32 = !bf;
+  if (bf && part_bytes) {
+    g.part = (float*)part;
+    g.part_bytes = part_bytes;
+  }
   return hip_status(bf ? tpk::launch_gemm_bf16(g, s) : tpk::launch_gemm_f32(g, s), "column-parallel GEMM launch");
 }
 
@@ -176,17 +188,20 @@ int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* 
                      void* hip_stream) {
   TRY(check_ffn("tp_ffn_shard_fwd", x, w1, w3, w2, nullptr, y_t, T, d, d_ff, T_p, t, act, in_dtype,
                 out_dtype, true, true));
+  const size_t elt = in_dtype == TP_BF16 ? 2 : 4;
+  const size_t hbytes = round256((size_t)T * (size_t)(d_ff / T_p) * elt);   // H(t): required
   if (T > 0) {
     if (!workspace) return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace is NULL");
     if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
-    if (workspace_bytes < need)
-      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (workspace_bytes < hbytes)
+      return fail(TP_ERR_WORKSPACE, "tp_ffn_shard_fwd: workspace %zu bytes < %zu needed", workspace_bytes, hbytes);
   }
   if (T == 0) return TP_OK;
   hipStream_t s = (hipStream_t)hip_stream;
   const bool bf = in_dtype == TP_BF16;
-  TRY(launch_column(x, w1, w3, workspace, T, d, d_ff, T_p, t, act, bf, s));
+  // bytes beyond H(t) serve as the column product's split-K scratch
+  TRY(launch_column(x, w1, w3, workspace, T, d, d_ff, T_p, t, act, bf, s, (char*)workspace + hbytes,
+                    workspace_bytes - hbytes));
   return launch_row(workspace, w2, y_t, T, d, d_ff, T_p, t, bf, out_dtype == TP_F32, s);
 }
 
@@ -229,7 +244,8 @@ int tp_ffn_shard_fwd_noalloc(const void* x, const void* w1, const void* w3, cons
   const char* fn = "tp_ffn_shard_fwd_noalloc";
   TRY(check_ffn(fn, x, w1, w3, w2, nullptr, y_t, T, d, d_ff, T_p, t, act, in_dtype, out_dtype, true, true));
   if (T == 0) return TP_OK;
-  const size_t need = tp_ffn_workspace_bytes(T, d_ff, T_p, in_dtype);
+  const size_t elt = in_dtype == TP_BF16 ? 2 : 4;
+  const size_t need = round256((size_t)T * (size_t)(d_ff / T_p) * elt);
   if (need > TP_NOALLOC_SCRATCH_BYTES)
     return fail(TP_ERR_WORKSPACE, "%s: H(t) needs %zu bytes, above the %zu bytes of scratch held per GPU",
                 fn, need, (size_t)TP_NOALLOC_SCRATCH_BYTES);
@@ -237,7 +253,9 @@ int tp_ffn_shard_fwd_noalloc(const void* x, const void* w1, const void* w3, cons
   TRY(scratch_address(&h));
   hipStream_t s = (hipStream_t)hip_stream;
   const bool bf = in_dtype == TP_BF16;
-  TRY(launch_column(x, w1, w3, h, T, d, d_ff, T_p, t, act, bf, s));
+  // the rest of the scratch serves as the column product's split-K partial sums
+  TRY(launch_column(x, w1, w3, h, T, d, d_ff, T_p, t, act, bf, s, (char*)h + need,
+                    (size_t)TP_NOALLOC_SCRATCH_BYTES - need));
   return launch_row(h, w2, y_t, T, d, d_ff, T_p, t, bf, out_dtype == TP_F32, s);
 }
 
@@ -476,12 +494,32 @@ int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t, int64_
   return hip_status(bf ? tpk::launch_gemm_bf16(g, s) : tpk::launch_gemm_f32(g, s), "out-projection GEMM launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Q, K, V of a rank's heads [T, (h_t + 2 kv_t) head_dim] bf16, then the split-K scratch of
+// the fused projection when it is too small to fill the GPU (sized for a deep product: d
+// is not an argument of the queries).
+size_t heads_qkv_bytes(int64_t T, int64_t h_t, int64_t kv_t, int32_t head_dim) {
+  return round256((size_t)T * (size_t)((h_t + 2 * kv_t) * head_dim) * 2);
+}
+size_t heads_split_bytes(int64_t T, int64_t h_t, int64_t kv_t, int32_t head_dim) {
+  if ((h_t + 2 * kv_t) * head_dim > kMaxExtent || T >= kMaxRows) return 0;
+  const int32_t seg[3] = {(int32_t)(h_t * head_dim), (int32_t)(kv_t * head_dim), (int32_t)(kv_t * head_dim)};
+  return round256(tpk::splitk_scratch_bytes(T, 3, seg, int64_t(1) << 30, false));
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t tp_attn_heads_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
                                      int32_t n_kv_heads, int32_t head_dim, int32_t T_p) {
   if (n_seq < 0 || seq_len < 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || T_p < 1) return 0;
   if (n_heads % T_p || n_kv_heads % T_p) return 0;
-  const int64_t h_t = n_heads / T_p, kv_t = n_kv_heads / T_p;
-  return round256((size_t)(n_seq * seq_len) * (size_t)((h_t + 2 * kv_t) * head_dim) * 2);
+  const int64_t h_t = n_heads / T_p, kv_t = n_kv_heads / T_p, T = n_seq * seq_len;
+  return heads_qkv_bytes(T, h_t, kv_t, head_dim) + heads_split_bytes(T, h_t, kv_t, head_dim);
 }
 
 size_t tp_attn_heads_kvrep_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
@@ -491,7 +529,8 @@ size_t tp_attn_heads_kvrep_workspace_bytes(int64_t n_seq, int64_t seq_len, int32
     return tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
   if (n_heads % T_p || T_p % n_kv_heads || n_heads % n_kv_heads) return 0;
   // one (replicated) KV head per rank
-  return round256((size_t)(n_seq * seq_len) * (size_t)((n_heads / T_p + 2) * head_dim) * 2);
+  const int64_t h_t = n_heads / T_p, T = n_seq * seq_len;
+  return heads_qkv_bytes(T, h_t, 1, head_dim) + heads_split_bytes(T, h_t, 1, head_dim);
 }
 
 }  // extern "C"
@@ -541,8 +580,8 @@ int attn_heads_impl(const char* fn, bool kvrep, const void* x, const void* wq, c
   TRY(check_ptr(wk, "wk"));
   TRY(check_ptr(wv, "wv"));
   TRY(check_ptr(o_t, "o_t"));
-  const size_t need = kvrep ? tp_attn_heads_kvrep_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p)
-                            : tp_attn_heads_workspace_bytes(n_seq, seq_len, n_heads, n_kv_heads, head_dim, T_p);
+  // Q, K, V are required; bytes beyond them serve as the projection's split-K scratch
+  const size_t need = heads_qkv_bytes(T, h_t, kv_t, head_dim);
   if (T > 0) {
     if (!workspace) return fail(TP_ERR_WORKSPACE, "%s: workspace is NULL", fn);
     if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -578,6 +617,10 @@ int attn_heads_impl(const char* fn, bool kvrep, const void* x, const void* wq, c
     g.Nx[i] = (int32_t)(kv_t * head_dim);
     g.ldbx[i] = (int32_t)(n_kv_heads * head_dim);
     g.ldcx[i] = g.Nx[i];
+  }
+  if (workspace_bytes > need) {
+    g.part = (float*)((char*)workspace + need);
+    g.part_bytes = workspace_bytes - need;
   }
   TRY(hip_status(tpk::launch_gemm_bf16(g, s), "QKV projection GEMM launch"));
   tpk::AttnDesc a{};

@@ -221,11 +221,20 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  // column segment of this tile (all values wave-uniform)
+  // split-K: workgroups [s * tiles, (s + 1) * tiles) take k range s (forward layout only)
+  int split = 0, bid = blockIdx.x;
+  const bool splitk = LAYOUT == kNN && g.ksplit > 1;
+  if (splitk) {
+    split = bid / (tiles_m * tiles_n);
+    bid -= split * tiles_m * tiles_n;
+  }
+  map_tile(bid, tiles_m, tiles_n, tm, tn);
+  // column segment of this tile (all values wave-uniform); pcol0: its first column in
+  // the split-K partial rows
   const void* Bseg = g.B0;
   void* Cseg = g.C;
   int N_ = g.N, ldb_ = g.ldb, ldc_ = g.ldc;
+  int pcol0 = 0;
   if (!DUAL && g.nseg > 1) {
     const int t0 = (g.N + BNS - 1) / BNS;
     if (tn >= t0) {
@@ -238,23 +247,27 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
       N_ = g.Nx[sg];
       ldb_ = g.ldbx[sg];
       ldc_ = g.ldcx[sg];
+      pcol0 = g.N + (sg ? g.Nx[0] : 0);
     }
   }
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BNS;
   const int64_t rows_left64 = g.M - m0;
   const int rows_left = rows_left64 < BM ? (int)rows_left64 : BM;
+  // k range of this workgroup
+  const int kbeg = splitk ? split * g.kchunk : 0;
+  const int Kv = splitk ? (g.K - kbeg < g.kchunk ? g.K - kbeg : g.kchunk) : g.K;
 
   // Tile origins; a k-tile then advances by k0 (k-contiguous) or k0 rows (m/n-contiguous).
-  const int64_t a_org = A_KC ? m0 * g.lda : m0;
-  const int64_t b_org = B_KC ? (int64_t)n0 * ldb_ : n0;
+  const int64_t a_org = A_KC ? m0 * g.lda + kbeg : m0;
+  const int64_t b_org = B_KC ? (int64_t)n0 * ldb_ : n0 + (int64_t)kbeg * ldb_;
   const __bf16* A = (const __bf16*)g.A + a_org;
   const __bf16* B0 = (const __bf16*)Bseg + b_org;
-  const __bf16* B1 = DUAL ? (const __bf16*)g.B1 + n0 : B0;
+  const __bf16* B1 = DUAL ? (const __bf16*)g.B1 + n0 + (int64_t)kbeg * ldb_ : B0;
   // second k segment (kNT): same origins in A2/B2
   const __bf16* A2 = LAYOUT == kNT && g.A2 ? (const __bf16*)g.A2 + a_org : A;
   const __bf16* B2 = LAYOUT == kNT && g.B2 ? (const __bf16*)g.B2 + b_org : B0;
-  const int nk0 = LAYOUT == kNT ? (g.K + BK - 1) / BK : 0x7FFFFFFF;
+  const int nk0 = LAYOUT == kNT ? (Kv + BK - 1) / BK : 0x7FFFFFFF;
 
   // ---- per-lane global->LDS descriptors (fixed over the k loop).  Lanes whose row (A)
   // or column (B) lies outside the matrix get an out-of-range offset once and for all;
@@ -302,7 +315,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   // Copies [first, first + count) of stage kt's LPS per wave (A copies first, then B).
   auto issue_range = [&](int kt, LDS_AS unsigned char* base, int first, int count) {
     int k0 = kt * BK;
-    int Kc = g.K;
+    int Kc = Kv;
     const __bf16* Ab = A;
     const __bf16* Bb = b_second ? B1 : B0;
     if constexpr (LAYOUT == kNT) {
@@ -448,7 +461,7 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   bf16x8 bfr[2][NB];
   // k-tiles, padded to a multiple of NST: tiles past K load as zeros (every copy
   // out of range), so every stage runs the same branch-free product code.
-  const int nk_all = LAYOUT == kNT ? nk0 + (g.K2 + BK - 1) / BK : (g.K + BK - 1) / BK;
+  const int nk_all = LAYOUT == kNT ? nk0 + (g.K2 + BK - 1) / BK : (Kv + BK - 1) / BK;
   const int nk = (nk_all + NST - 1) / NST * NST;
 
   // prologue: NST stages in flight, then stage 0's first fragments
@@ -511,6 +524,29 @@ __global__ void __launch_bounds__(kThreads) gemm_bf16_kernel(GemmDesc g, int til
   }
   // the trailing zero-fill copies must land before this workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- split-K: this workgroup's fp32 partial product (U columns, then V columns of the
+  // gated pair), summed and finished by splitk_reduce_kernel
+  if (splitk) {
+    float* P = g.part + (int64_t)split * g.pslice;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * WTM + mb * 32 + (lane & 31);
+      if (r >= rows_left) continue;
+      float* prow = P + (m0 + r) * g.pld + pcol0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WCOLS + (nb % NBS) * 32 + 8 * q + 4 * (lane >> 5);
+          if (n >= N_) continue;
+          const f32x16& a = acc[mb][nb];
+          *(f32x4*)(prow + (DUAL && nb >= NBS ? g.N : 0) + n) =
+              f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+    }
+    return;
+  }
 
   // ---- bf16 outputs through LDS.  Each lane holds 4 consecutive columns of 16 rows per
   // accumulator block, so direct stores write 8 bytes into each of 32 rows per
@@ -659,9 +695,149 @@ hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
   const int64_t tm = (g.M + BM - 1) / BM;
   int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
   for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) tn += (g.Nx[i] + OUT_BN - 1) / OUT_BN;
-  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t ks = LAYOUT == kNN && g.ksplit > 1 ? g.ksplit : 1;
+  if (tm * tn * ks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, DUAL, ACT, OUT_F32, LAYOUT, SAVE>),
-                     dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, g, (int)tm, (int)tn);
+                     dim3((unsigned)(tm * tn * ks)), dim3(kThreads), 0, s, g, (int)tm, (int)tn);
+  return hipGetLastError();
+}
+
+// ---- split-K for products too small to fill the GPU (a few thousand tokens): the k range
+// is split over S workgroups per output tile, each writing an fp32 partial product, and
+// splitk_reduce_kernel adds the S partials in split order (one rounding per sum, the same
+// order every call) and applies the epilogue.  Output columns live in up to three
+// segments (the fused Q, K, V projections).
+struct SplitOut {
+  void* C[3];
+  int32_t ldc[3];
+  int32_t ncol[3];
+  int32_t nseg;
+};
+
+template <int ACT, bool GATED>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* part, int S, int64_t pslice, int pld,
+                                                            int64_t M, int N, SplitOut o) {
+  const int cpr = N / 8;   // 8-column chunks per output row
+  const int64_t total = M * cpr;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t m = idx / cpr;
+    const int c = (int)(idx - m * cpr) * 8;
+    const float* p = part + m * pld + c;
+    f32x4 u0 = *(const f32x4*)p, u1 = *(const f32x4*)(p + 4);
+    f32x4 v0 = f32x4{}, v1 = f32x4{};
+    if constexpr (GATED) {
+      v0 = *(const f32x4*)(p + N);
+      v1 = *(const f32x4*)(p + N + 4);
+    }
+    for (int sp = 1; sp < S; ++sp) {
+      const float* q = p + sp * pslice;
+      u0 += *(const f32x4*)q;
+      u1 += *(const f32x4*)(q + 4);
+      if constexpr (GATED) {
+        v0 += *(const f32x4*)(q + N);
+        v1 += *(const f32x4*)(q + N + 4);
+      }
+    }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = (__bf16)epilogue<ACT>(u0[e], v0[e]);
+      out[4 + e] = (__bf16)epilogue<ACT>(u1[e], v1[e]);
+    }
+    int seg = 0, cc = c;
+    if (o.nseg > 1 && cc >= o.ncol[0]) {
+      cc -= o.ncol[0];
+      seg = 1;
+      if (o.nseg > 2 && cc >= o.ncol[1]) {
+        cc -= o.ncol[1];
+        seg = 2;
+      }
+    }
+    *(bf16x8*)((__bf16*)o.C[seg] + m * o.ldc[seg] + cc) = out;
+  }
+}
+
+// Split plan: output tile width (256, or 192 when every segment is a multiple of 192; the
+// gated pair only 128 outputs of 256 accumulator columns) and S, chosen to fill the most
+// CUs with at most one workgroup each: tiles * S <= 256, each split at least 1,024 deep,
+// S <= 4.  Products with at least 192 tiles of 256 x 256 do not split.
+struct SplitPlan {
+  int bn;        // output columns per tile (0: no split)
+  int S;
+  int64_t tiles;
+  int64_t pld;   // partial row length
+};
+
+SplitPlan plan_split(int64_t M, int nseg, const int32_t* segN, int64_t K, bool gated) {
+  SplitPlan best{0, 1, 0, 0};
+  if (M < 1024 || K < 2048) return best;
+  int64_t ncols = 0;
+  bool div192 = !gated;
+  for (int i = 0; i < nseg; ++i) {
+    ncols += segN[i];
+    if (segN[i] % 192) div192 = false;
+  }
+  const int64_t tmr = (M + 255) / 256;
+  auto tiles_for = [&](int bn) {
+    int64_t t = 0;
+    for (int i = 0; i < nseg; ++i) t += (segN[i] + bn - 1) / bn;
+    return tmr * t;
+  };
+  const int64_t t_full = tiles_for(gated ? 128 : 256);
+  if (t_full >= 192) return best;
+  int64_t best_occ = 0;
+  for (int opt = 0; opt < 2; ++opt) {
+    const int bn = opt == 0 ? (gated ? 128 : 256) : 192;
+    if (opt == 1 && !div192) continue;
+    const int64_t t = tiles_for(bn);
+    int64_t S = 256 / t;
+    if (S > 4) S = 4;
+    while (S > 1 && K / S < 1024) --S;
+    if (S < 2) continue;
+    if (t * S > best_occ) {
+      best_occ = t * S;
+      best = SplitPlan{bn, (int)S, t, gated ? 2 * ncols : ncols};
+    }
+  }
+  return best;
+}
+
+template <bool DUAL, int ACT>
+hipError_t launch_split(const GemmDesc& g0, const SplitPlan& pl, hipStream_t s) {
+  GemmDesc g = g0;
+  g.ksplit = pl.S;
+  // k per split: a multiple of 64 so that every split starts on a whole k-tile
+  g.kchunk = (int32_t)(((int64_t)g.K + pl.S * 64 - 1) / (pl.S * 64) * 64);
+  g.pld = (int32_t)pl.pld;
+  g.pslice = g.M * pl.pld;
+  hipError_t e;
+  const bool long_k = g.kchunk > 2048;
+  e = hipErrorInvalidValue;
+  if (!DUAL && pl.bn == 192) {
+    if constexpr (!DUAL)
+      e = long_k ? launch_cfg<256, 192, 32, 4, DUAL, ACT, false, kNN, false>(g, s)
+                 : launch_cfg<256, 192, 64, 2, DUAL, ACT, false, kNN, false>(g, s);
+  } else {
+    e = long_k ? launch_cfg<256, 256, 32, 4, DUAL, ACT, false, kNN, false>(g, s)
+               : launch_cfg<256, 256, 64, 2, DUAL, ACT, false, kNN, false>(g, s);
+  }
+  if (e != hipSuccess) return e;
+  SplitOut o{};
+  o.nseg = DUAL ? 1 : g.nseg;
+  o.C[0] = g.C;
+  o.ldc[0] = g.ldc;
+  o.ncol[0] = g.N;
+  for (int i = 0; i + 1 < o.nseg; ++i) {
+    o.C[i + 1] = g.Cx[i];
+    o.ldc[i + 1] = g.ldcx[i];
+    o.ncol[i + 1] = g.Nx[i];
+  }
+  const int64_t ntot = DUAL ? g.N : pl.pld;
+  const int64_t chunks = g.M * (ntot / 8);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL((splitk_reduce_kernel<ACT, DUAL>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const float*)g.part, pl.S, g.pslice, g.pld, g.M, (int)ntot, o);
   return hipGetLastError();
 }
 
@@ -674,6 +850,17 @@ hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
 template <bool DUAL, int ACT, bool OUT_F32, int LAYOUT = kNN, bool SAVE = false>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
+  if constexpr (LAYOUT == kNN && !OUT_F32 && !SAVE) {
+    if (g.part) {
+      int32_t segN[3] = {g.N, g.Nx[0], g.Nx[1]};
+      const int nseg = DUAL ? 1 : g.nseg;
+      const SplitPlan pl = plan_split(g.M, nseg, segN, g.K, DUAL);
+      bool ok = pl.bn > 0;
+      for (int i = 0; i < nseg && ok; ++i) ok = segN[i] % 8 == 0;
+      if (ok && (size_t)pl.S * (size_t)g.M * (size_t)pl.pld * 4 <= g.part_bytes)
+        return launch_split<DUAL, ACT>(g, pl, s);
+    }
+  }
   int64_t ncols = g.N;
   for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) ncols += g.Nx[i];
   const int64_t big = ((g.M + 255) / 256) * ((ncols + OUT_BN - 1) / OUT_BN);
@@ -738,6 +925,12 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t splitk_scratch_bytes(int64_t M, int nseg, const int32_t* segN, int64_t K, bool gated) {
+  const SplitPlan pl = plan_split(M, nseg, segN, K, gated);
+  if (pl.bn == 0) return 0;
+  return (size_t)pl.S * (size_t)M * (size_t)pl.pld * 4;
+}
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.out_f32) {

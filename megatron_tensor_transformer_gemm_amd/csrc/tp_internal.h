@@ -39,7 +39,25 @@ struct GemmDesc {
   void* V = nullptr;
   void* dV = nullptr;
   int32_t ldu = 0;
+  // Split-K (forward layout, bf16 outputs, no saved pre-activations): when `part` is
+  // non-null the launcher may split the k range over `ksplit` workgroups per tile; each
+  // writes its fp32 partial product into part + split * pslice ([M, pld] with pld the
+  // total output width, doubled for the gated pair: U columns then V columns), and a
+  // second kernel sums the partials in split order and applies the epilogue.
+  // part_bytes bounds what the launcher may use.
+  float* part = nullptr;
+  size_t part_bytes = 0;
+  int32_t ksplit = 1;   // set by the launcher
+  int32_t kchunk = 0;   // k per split (a multiple of the stage depth), set by the launcher
+  int64_t pslice = 0;   // elements per split, set by the launcher
+  int32_t pld = 0;      // partial row length, set by the launcher
 };
+
+// Split-K scratch (bytes) the forward launcher uses for a bf16 product of M rows, k depth
+// K and nseg column segments of segN[i] outputs (gated: one segment, 2N accumulator
+// columns): 0 when the product fills the GPU without splitting.  With K unknown, pass a
+// large K: the launcher never needs more than that bound.
+size_t splitk_scratch_bytes(int64_t M, int nseg, const int32_t* segN, int64_t K, bool gated);
 
 // bf16 inputs, fp32 accumulation on MFMA; output bf16 (or fp32 if out_f32).
 // A [M, K] and B [K, N], both row-major; the activation `act` in the epilogue.

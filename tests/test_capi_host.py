@@ -50,11 +50,21 @@ def test_workspace_queries():
     assert S.tp_ffn_workspace_bytes(3, 24, 8, S.TP_BF16) == 256          # rounded up
     assert S.tp_ffn_workspace_bytes(64, 1024, 2, S.TP_F32) == 64 * 512 * 4
     assert S.tp_ffn_workspace_bytes(64, 1000, 3, S.TP_BF16) == 0
+    # the Llama-shaped ranks fill the GPU without splitting; the GPT block's 2048-token FFN
+    # column product (128 tiles of 256 x 192) splits k two ways: 2 fp32 copies of [2048, 3072]
+    assert S.tp_ffn_workspace_bytes(16384, 28672, 8, S.TP_BF16) == 16384 * 3584 * 2
+    assert S.tp_ffn_workspace_bytes(2048, 24576, 8, S.TP_BF16) == 2048 * 3072 * 2 + 2 * 2048 * 3072 * 4
+    assert S.tp_ffn_workspace_bytes(2048, 24576, 8, S.TP_F32) == 2048 * 3072 * 4
     assert S.tp_ffn_workspace_bytes(64, 1024, 2, 7) == 0
-    assert S.tp_attn_heads_workspace_bytes(1, 2048, 48, 48, 128, 8) == 2048 * 18 * 128 * 2
+    # the GPT block's 2048-token rank: Q, K, V (18 heads of 128), then split-K scratch for the
+    # fused projection (72 tiles of 256 x 256 over 3 k-splits: 3 fp32 copies of [2048, 2304])
+    assert S.tp_attn_heads_workspace_bytes(1, 2048, 48, 48, 128, 8) == 2048 * 18 * 128 * 2 + 3 * 2048 * 2304 * 4
     assert S.tp_attn_heads_workspace_bytes(1, 2048, 64, 8, 128, 16) == 0
-    # TP16 over 8 KV heads: 4 query heads and one replicated KV head per rank
-    assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 64, 8, 128, 16) == 2048 * 6 * 128 * 2
+    # TP16 over 8 KV heads: 4 query heads and one replicated KV head per rank; the projection
+    # (32 tiles) splits 4 ways
+    assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 64, 8, 128, 16) == 2048 * 6 * 128 * 2 + 4 * 2048 * 768 * 4
+    # short sequences are not split
+    assert S.tp_attn_heads_workspace_bytes(2, 200, 8, 4, 64, 2) == 400 * 8 * 64 * 2
     assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 64, 8, 128, 8) == \
         S.tp_attn_heads_workspace_bytes(1, 2048, 64, 8, 128, 8)
     assert S.tp_attn_heads_kvrep_workspace_bytes(1, 2048, 48, 6, 128, 16) == 0
