@@ -818,10 +818,9 @@ hipError_t launch_split(const GemmDesc& g0, const SplitPlan& pl, hipStream_t s) 
   hipError_t e;
   const bool long_k = g.kchunk > 2048;   // 192-column tiles: 32-k stages (8 waves need 64-k ones)
   e = hipErrorInvalidValue;
+  (void)long_k;
   if (!DUAL && pl.bn == 192) {
-    if constexpr (!DUAL)
-      e = long_k ? launch_cfg<256, 192, 32, 4, DUAL, ACT, false, kNN, false>(g, s)
-                 : launch_cfg<256, 192, 64, 2, DUAL, ACT, false, kNN, false, 8>(g, s);
+    if constexpr (!DUAL) e = launch_cfg<256, 192, 64, 2, DUAL, ACT, false, kNN, false, 8>(g, s);
   } else {
     e = launch_cfg<256, 256, 64, 2, DUAL, ACT, false, kNN, false, 8>(g, s);
   }
@@ -888,9 +887,8 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
       const int64_t c192 = g.N / 192;
       const int64_t t256 = ((g.M + 255) / 256) * c192, t128 = ((g.M + 127) / 128) * c192;
       if (t256 >= 224 && t256 <= 256) {
-        if (kdepth > 2048) return launch_cfg<256, 192, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
-        // short k (the GPT block's out-projection, k = 768): 8 waves, 23.1 against 25.0 us alone
         if constexpr (!SAVE) return launch_cfg<256, 192, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
+        else if (kdepth > 2048) return launch_cfg<256, 192, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
         else return launch_cfg<256, 192, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
       }
       if (t128 >= 224 && t128 <= 256) {
