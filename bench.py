@@ -739,20 +739,41 @@ def measure_block(steps: int, warmup: int) -> dict:
         for i, nm in enumerate(names):
             dur.setdefault(nm, []).append(ev[s_][i].elapsed_time(ev[s_][i + 1]))
     avg = {k: 1e3 * sum(v) / len(v) for k, v in dur.items()}
-    # the attention core alone, on the last rank's projected heads
+
+    def replay_ms(fn, reps):
+        """fn captured once as a graph, replayed `reps` times: GPU time per replay in ms,
+        free of the host's per-call overhead (which exceeds some of these kernels)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(2):
+            graph.replay()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record()
+        for _ in range(reps):
+            graph.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / reps
+
+    ms_graph = replay_ms(step, steps)
+    # the attention core alone, on the last rank's projected heads: 20 calls in one graph
     q = ws.view(torch.bfloat16)
     qv = q[: L * kdim]
     kv = q[L * kdim: 2 * L * kdim]
     vv = q[2 * L * kdim: 3 * L * kdim]
-    for _ in range(3):
-        S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
-    e1.record()
-    torch.cuda.synchronize()
-    core_us = e0.elapsed_time(e1) * 1e3 / 20
+
+    def cores():
+        for _ in range(20):
+            S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
+    core_us = replay_ms(cores, 5) * 1e3 / 20
     fl_qkv = 2.0 * L * d * 3 * kdim
     fl_core = 2.0 * h_t * dh * L * (L + 1)
     fl_out = 2.0 * L * kdim * d
@@ -763,12 +784,15 @@ def measure_block(steps: int, warmup: int) -> dict:
     def tf(fl, us):
         return round(fl / (us * 1e-6) / 1e12, 1)
     res = {
-        "workload": w.name, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
-        "tflops": round(fl_step / (ms * 1e-3) / 1e12, 2), "step_flops": fl_step,
+        "workload": w.name, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_graph, 4),
+        "timing": "graph replay of the whole step (per-kernel times below: eager, HIP events)",
+        "tflops": round(fl_step / (ms_graph * 1e-3) / 1e12, 2), "step_flops": fl_step,
+        "eager_ms_per_step": round(ms, 4), "eager_tflops": round(fl_step / (ms * 1e-3) / 1e12, 2),
         "kernels": {
             "qkv_projection_plus_attention_core": {"avg_us": round(avg["attn_heads"], 2),
                                                    "tflops": tf(fl_qkv + fl_core, avg["attn_heads"])},
             "attention_core_causal": {"avg_us": round(core_us, 2), "tflops": tf(fl_core, core_us),
+                                      "timing": "20 calls replayed as one graph",
                                       "frac_peak": round(fl_core / (core_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "attn_outproj_gemm": {"avg_us": round(avg["outproj"], 2), "tflops": tf(fl_out, avg["outproj"])},
             "ffn_shard_gelu": {"avg_us": round(avg["ffn"], 2), "tflops": tf(fl_ffn1 + fl_ffn2, avg["ffn"]),
@@ -777,7 +801,8 @@ def measure_block(steps: int, warmup: int) -> dict:
             "partial_sum_residual": {"avg_us": round(avg["psum"], 2)},
         },
     }
-    log(f"[bench] block: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; attention core {core_us:.1f} us")
+    log(f"[bench] block: {ms_graph:.3f} ms/step as a graph, {res['tflops']} TFLOP/s (eager {ms:.3f} ms); "
+        f"attention core {core_us:.1f} us")
     return res
 
 

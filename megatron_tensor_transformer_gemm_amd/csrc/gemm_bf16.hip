@@ -10,13 +10,18 @@
 // rank ("Tensor & Pipeline Parallelism", S17 diagram: the activation is
 // element-wise, so the sharded hidden state needs no communication).
 //
-// Design (one workgroup = 4 waves = 256 threads per output tile):
+// Design (one workgroup per output tile: 4 waves, or for the forward products 8 waves,
+// two per SIMD, so that one wave of a SIMD multiplies while the other issues copies):
 //  * HBM/L2 -> LDS with buffer_load ... lds (16 B per lane): no staging VGPRs,
 //    out-of-range rows/columns/k come back as zeros from the buffer
 //    descriptor's range check (masked lanes get an out-of-range offset), so
 //    ragged M, N and K need no separate edge code.
 //  * Two to four LDS stages in flight: later k-tiles stream in while the current
-//    one is multiplied.
+//    one is multiplied.  In the forward layout the next stage's copies are issued one
+//    at a time between the MFMAs of a stage's last substep.
+//  * Products too small to fill the GPU split k over several workgroups per tile
+//    (fp32 partials in the caller's workspace, summed in split order by a second
+//    kernel that applies the activation).
 //  * A fragments: ds_read_b128 of 8 consecutive k of one row.
 //  * B fragments: B is N-contiguous in memory and in LDS; ds_read_b64_tr_b16
 //    transposes 4 k-rows x 16 columns per 16-lane group on the way to the
@@ -815,10 +820,8 @@ hipError_t launch_split(const GemmDesc& g0, const SplitPlan& pl, hipStream_t s) 
   g.kchunk = (int32_t)(((int64_t)g.K + pl.S * 64 - 1) / (pl.S * 64) * 64);
   g.pld = (int32_t)pl.pld;
   g.pslice = g.M * pl.pld;
-  hipError_t e;
-  const bool long_k = g.kchunk > 2048;   // 192-column tiles: 32-k stages (8 waves need 64-k ones)
-  e = hipErrorInvalidValue;
-  (void)long_k;
+  // 8 waves with two 64-deep stages, as the unsplit forward tiles
+  hipError_t e = hipErrorInvalidValue;
   if (!DUAL && pl.bn == 192) {
     if constexpr (!DUAL) e = launch_cfg<256, 192, 64, 2, DUAL, ACT, false, kNN, false, 8>(g, s);
   } else {
@@ -844,12 +847,15 @@ hipError_t launch_split(const GemmDesc& g0, const SplitPlan& pl, hipStream_t s) 
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 tiles once they give at least one full wave of workgroups over the
-// 256 CUs, else 128x128 (or 128x256 for the gated pair).  Long k-loops use 4 stages of 32 k
-// (more copies in flight); short ones 2 stages of 64 k (fewer, longer stages).  With both
-// operands k-contiguous (kNT) every tile row is a k-run in memory, and 64-k stages fetch
-// whole 128-byte lines: measured 2-5% faster than 32-k stages at every depth; there a last
-// wave of 256x256 tiles at most 3/4 full switches to 128x256 tiles.
+// Tile choice.  A forward product (bf16 output, no kept pre-activations) given split-K
+// scratch takes the split path when plan_split finds one.  Otherwise 256x256 tiles once they
+// give at least one full wave of workgroups over the 256 CUs (forward: 8 waves, two 64-k
+// stages; other layouts: 4 waves, 4 stages of 32 k for long k-loops, 2 of 64 k for short
+// ones), with smaller tiles below that (the forward rules further down), else 128x128 (or
+// 128x256 for the gated pair).  With both operands k-contiguous (kNT) every tile row is a
+// k-run in memory, and 64-k stages fetch whole 128-byte lines: measured 2-5% faster than
+// 32-k stages at every depth; there a last wave of 256x256 tiles at most 3/4 full switches
+// to 128x256 tiles.
 template <bool DUAL, int ACT, bool OUT_F32, int LAYOUT = kNN, bool SAVE = false>
 hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? 128 : 256;
