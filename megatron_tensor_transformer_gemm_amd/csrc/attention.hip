@@ -234,18 +234,11 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
         vf[hf][d] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
   };
-  // S^T of one block as two independent accumulation chains (even and odd k-steps), added
-  // at the end: a chain of dependent MFMAs on one accumulator waits for each result, and
-  // this one sits on the critical path of every key iteration (measured, L = 2048 / 8192
-  // causal, 6 heads of 128: 25.0 -> 21.3 us, 146 -> 118 us; four chains: slower, 242 VGPRs).
   auto qk = [&](const bf16x8 (&kf)[KS]) {
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks + 1], qf[ks + 1], s1, 0, 0, 0);
-    }
-    return s0 + s1;
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    return s;
   };
   auto pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pf)[2]) {
 #pragma unroll
