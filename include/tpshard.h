@@ -91,9 +91,14 @@ const char* tp_last_error(void);
 int tp_shard_range(int64_t extent, int32_t T_p, int32_t t, int64_t* begin, int64_t* len);
 
 /*
- * Bytes of device workspace tp_ffn_shard_fwd needs to hold H(t):
- * T * (d_ff/T_p) * sizeof(element of in_dtype), rounded up to 256 bytes.
- * Returns 0 for invalid arguments (and for T == 0).
+ * Bytes of device workspace for tp_ffn_shard_fwd: H(t), T * (d_ff/T_p) *
+ * sizeof(element of in_dtype) rounded up to 256 bytes, followed, for bf16 products
+ * too small to fill the GPU (a few thousand tokens), by scratch for the column
+ * product's split-K: S fp32 partial products [S][T][d_ff/T_p] (twice as wide for
+ * SWIGLU/BILINEAR), S <= 4, rounded up to 256 bytes; d is not an argument, so the
+ * scratch is sized for the largest S any depth allows.  Shapes that never split
+ * (e.g. 16384 tokens, or fp32) get H(t) alone.  Returns 0 for invalid arguments
+ * (and for T == 0).
  */
 size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_dtype);
 
@@ -114,6 +119,14 @@ size_t tp_ffn_workspace_bytes(int64_t T, int64_t d_ff, int32_t T_p, int32_t in_d
  * fused into its epilogue, then the row-parallel GEMM.  No communication.
  * Errors: TP_ERR_INVALID_ARG, TP_ERR_NOT_DIVISIBLE (d_ff % T_p),
  * TP_ERR_WORKSPACE, TP_ERR_UNSUPPORTED, TP_ERR_HIP.
+ *
+ * Workspace: at least H(t)'s bytes (TP_ERR_WORKSPACE below that).  With the
+ * whole query size, a bf16 column product that cannot fill the GPU runs split
+ * over k: each split writes fp32 partials into the scratch after H(t) and a
+ * second kernel adds them in split order (the same order on every call, so
+ * results repeat bit for bit) and applies the activation; three kernels are
+ * enqueued then.  With only H(t)'s bytes the unsplit product runs.  The two
+ * differ only in fp32 summation order.
  */
 int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* w2,
                      void* y_t, void* workspace, size_t workspace_bytes,
@@ -128,6 +141,8 @@ int tp_ffn_shard_fwd(const void* x, const void* w1, const void* w3, const void* 
  * file-scope device array of TP_NOALLOC_SCRATCH_BYTES (128 MiB), kept until the
  * process ends; its address is looked up once per device, on the first call with
  * that device current.  The call itself allocates and frees nothing.
+ * The array's bytes past H(t) serve as the column product's split-K scratch
+ * when they hold it (else that product runs unsplit).
  *
  *   T * (d_ff/T_p) * sizeof(element of in_dtype), rounded up to 256 bytes, must
  *   not exceed TP_NOALLOC_SCRATCH_BYTES (TP_ERR_WORKSPACE otherwise; y_t untouched).
@@ -254,9 +269,13 @@ int tp_attn_outproj_shard_fwd(const void* o_t, const void* wo, void* y_t,
                               int32_t in_dtype, int32_t out_dtype, void* hip_stream);
 
 /*
- * Bytes of device workspace tp_attn_heads_shard_fwd needs (the rank's Q, K
- * and V): n_seq*seq_len * (h_t + 2*kv_t) * head_dim * 2, rounded up to 256.
- * Returns 0 for invalid arguments.
+ * Bytes of device workspace for tp_attn_heads_shard_fwd: the rank's Q, K and V,
+ * n_seq*seq_len * (h_t + 2*kv_t) * head_dim * 2 rounded up to 256, followed, when
+ * the fused Q/K/V product is too small to fill the GPU, by split-K scratch: S fp32
+ * partials [S][n_seq*seq_len][(h_t + 2*kv_t)*head_dim], S <= 4, rounded up to 256.
+ * tp_attn_heads_shard_fwd accepts any workspace of at least the Q, K, V bytes and
+ * splits only when the scratch fits (as tp_ffn_shard_fwd).  Returns 0 for invalid
+ * arguments.
  */
 size_t tp_attn_heads_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
                                      int32_t n_kv_heads, int32_t head_dim, int32_t T_p);
@@ -301,7 +320,8 @@ int tp_attn_heads_shard_fwd_kvrep(const void* x, const void* wq, const void* wk,
                                   int32_t T_p, int32_t t, int32_t causal, void* hip_stream);
 
 /* Workspace of tp_attn_heads_shard_fwd_kvrep: Q of the h_t query heads, K and V of the
- * rank's KV heads (one when replicated), n_seq*seq_len rows, bf16, rounded up to 256.
+ * rank's KV heads (one when replicated), n_seq*seq_len rows, bf16, rounded up to 256,
+ * then split-K scratch as for tp_attn_heads_workspace_bytes when the product splits.
  * 0 for invalid arguments. */
 size_t tp_attn_heads_kvrep_workspace_bytes(int64_t n_seq, int64_t seq_len, int32_t n_heads,
                                            int32_t n_kv_heads, int32_t head_dim, int32_t T_p);
