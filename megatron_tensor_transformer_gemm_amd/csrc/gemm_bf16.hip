@@ -10,8 +10,8 @@
 // rank ("Tensor & Pipeline Parallelism", S17 diagram: the activation is
 // element-wise, so the sharded hidden state needs no communication).
 //
-// Design (one workgroup per output tile: 4 waves, or for the forward products 8 waves,
-// two per SIMD, so that one wave of a SIMD multiplies while the other issues copies):
+// Design (one workgroup per output tile: 8 waves, two per SIMD, so that one wave of a
+// SIMD multiplies while the other issues copies; small-tile fallbacks keep 4 waves):
 //  * HBM/L2 -> LDS with buffer_load ... lds (16 B per lane): no staging VGPRs,
 //    out-of-range rows/columns/k come back as zeros from the buffer
 //    descriptor's range check (masked lanes get an out-of-range offset), so
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   };
   static_assert(A_BYTES % (1024 * NW) == 0 && (NSUB * SUB_BYTES) % (1024 * NW) == 0,
                 "copies split evenly over the waves");
-  static_assert(NW == 4 || (NW == 8 && LAYOUT == kNN), "8 waves: forward tiles");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BM % (32 * WMG) == 0, "whole 32-row blocks per wave");
   static_assert(KSUB % 2 == 0 && (ACPR == 4 || ACPR == 8), "BK must be 32 or 64");
   static_assert(NST >= 2 && NST <= 5 && (NST - 1) * LPS <= 63, "stages");
@@ -849,10 +849,10 @@ hipError_t launch_split(const GemmDesc& g0, const SplitPlan& pl, hipStream_t s) 
 
 // Tile choice.  A forward product (bf16 output, no kept pre-activations) given split-K
 // scratch takes the split path when plan_split finds one.  Otherwise 256x256 tiles once they
-// give at least one full wave of workgroups over the 256 CUs (forward: 8 waves, two 64-k
-// stages; other layouts: 4 waves, 4 stages of 32 k for long k-loops, 2 of 64 k for short
-// ones), with smaller tiles below that (the forward rules further down), else 128x128 (or
-// 128x256 for the gated pair).  With both operands k-contiguous (kNT) every tile row is a
+// give at least one full wave of workgroups over the 256 CUs, on 8 waves (two 64-k stages;
+// the weight-gradient (kTN) products four 32-k stages for long k-loops), with smaller tiles
+// below that (the forward rules further down), else 128x128 (or 128x256 for the gated
+// pair) on 4 waves.  With both operands k-contiguous (kNT) every tile row is a
 // k-run in memory, and 64-k stages fetch whole 128-byte lines: measured 2-5% faster than
 // 32-k stages at every depth; there a last wave of 256x256 tiles at most 3/4 full switches
 // to 128x256 tiles.
@@ -879,8 +879,10 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
       const int64_t last = big % 256;
       // 128x256 tiles leave LDS for a third 64-deep stage (3 x 48 KiB); measured on the 70B
       // dH product (1,792 tiles): 1,171 -> 1,089 us against two stages
-      if (last != 0 && last <= 192) return launch_cfg<128, 256, 64, 3, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
-      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      // 8 waves, as the forward tiles (70B backward, same box: 43.3-44.0 -> 42.2 ms per step
+      // together with the TN products below; either layout alone gained less)
+      if (last != 0 && last <= 192) return launch_cfg<128, 256, 64, 3, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
+      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
     }
   }
   if constexpr (LAYOUT == kNN && !DUAL) {
@@ -939,9 +941,15 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     // against 754 us, out-projection 257-261 against 273 us (two 64-deep stages).
     if constexpr (LAYOUT == kNN && !SAVE) {
       return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
+    } else if constexpr (LAYOUT == kTN) {
+      // the weight gradients: 8 waves with four 32-deep stages (two 64-deep ones measured
+      // 2.5 % slower over the backward step)
+      if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
+      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
     } else {
-      if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
-      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
+      // the training forward, which also stores U (and V): 8 waves, two 64-deep stages
+      // (70B column GEMM + row GEMM of one rank: 2,383-2,397 -> 2,324-2,327 us)
+      return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
     }
   }
   return launch_cfg<128, DUAL ? 256 : 128, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);

@@ -56,11 +56,14 @@ def _check_untouched(full: np.ndarray, lo: int, hi: int, axis: int, name: str):
 
 # ----------------------------------------------------------------------------- bit-exact offsets
 @pytest.mark.parametrize("act", ["none", "bilinear"])
-@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (4100, 1032, 2, 1288), (4100, 264, 1, 4000)],
-                         ids=["small-tiles", "large-tiles", "dH-128x256-3-stage"])
+@pytest.mark.parametrize("shape", [(300, 264, 4, 136), (4100, 1032, 2, 1288), (4100, 264, 1, 4000),
+                                   (4000, 4000, 1, 4000)],
+                         ids=["small-tiles", "large-tiles", "dH-128x256-3-stage", "full-wave-256x256"])
 def test_backward_integer_bit_exact(act, shape):
     """Integer inputs: dX(t) and the weight-gradient blocks (fp32) equal the oracle bit for bit,
-    and nothing outside the rank's blocks is written."""
+    and nothing outside the rank's blocks is written.  The last shape gives every product a
+    full wave of 256 x 256 tiles (16 x 16, ragged at 4000), the dispatch of the full-size
+    backward (8 waves; dW with four 32-deep stages)."""
     T, d, T_p, n = shape
     d_ff = T_p * n
     log(f"[bwd-integer] act={act} T={T} d={d} d_ff={d_ff} T_p={T_p}")
