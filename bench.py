@@ -740,30 +740,7 @@ def measure_block(steps: int, warmup: int) -> dict:
             dur.setdefault(nm, []).append(ev[s_][i].elapsed_time(ev[s_][i + 1]))
     avg = {k: 1e3 * sum(v) / len(v) for k, v in dur.items()}
 
-    def replay_ms(fn, reps):
-        """fn captured once as a graph, replayed `reps` times: GPU time per replay in ms,
-        free of the host's per-call overhead (which exceeds some of these kernels)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
-        for _ in range(2):
-            graph.replay()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a0.record()
-        for _ in range(reps):
-            graph.replay()
-        a1.record()
-        torch.cuda.synchronize()
-        return a0.elapsed_time(a1) / reps
-
-    ms_graph = replay_ms(step, steps)
+    ms_graph = graph_replay_ms(step, steps)
     # the attention core alone, on the last rank's projected heads: 20 calls in one graph
     q = ws.view(torch.bfloat16)
     qv = q[: L * kdim]
@@ -773,7 +750,7 @@ def measure_block(steps: int, warmup: int) -> dict:
     def cores():
         for _ in range(20):
             S.tp_attn_core_fwd(qv, kv, vv, o_t, 1, L, h_t, h_t, dh, kdim, kdim, kdim, True)
-    core_us = replay_ms(cores, 5) * 1e3 / 20
+    core_us = graph_replay_ms(cores, 5) * 1e3 / 20
     fl_qkv = 2.0 * L * d * 3 * kdim
     fl_core = 2.0 * h_t * dh * L * (L + 1)
     fl_out = 2.0 * L * kdim * d
@@ -804,6 +781,33 @@ def measure_block(steps: int, warmup: int) -> dict:
     log(f"[bench] block: {ms_graph:.3f} ms/step as a graph, {res['tflops']} TFLOP/s (eager {ms:.3f} ms); "
         f"attention core {core_us:.1f} us")
     return res
+
+
+def graph_replay_ms(fn, reps: int, warmup: int = 2) -> float:
+    """fn (launches only: no allocation, memset or synchronisation) captured once as a
+    graph and replayed `reps` times: GPU time per replay in ms, free of the host's
+    per-call overhead, which exceeds some of these kernels."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a0.record()
+    for _ in range(reps):
+        graph.replay()
+    a1.record()
+    torch.cuda.synchronize()
+    return a0.elapsed_time(a1) / reps
 
 
 def measure_ring(steps: int, warmup: int) -> dict:
@@ -850,19 +854,24 @@ def measure_ring(steps: int, warmup: int) -> dict:
         torch.cuda.synchronize()
         return 1e3 * e0.elapsed_time(e1) / steps
 
-    full_us = timed(full)
-    last_us = timed(lambda: ring([C - 1]))     # the most loaded rank: every chunk is visible
-    ring_us = timed(ring)
+    # graph replays (several of these kernels are shorter than a host call), eager beside them
+    eager_ring_us = timed(ring)
+    full_us = 1e3 * graph_replay_ms(full, steps, warmup)
+    last_us = 1e3 * graph_replay_ms(lambda: ring([C - 1]), steps, warmup)   # every chunk visible
+    ring_us = 1e3 * graph_replay_ms(ring, steps, warmup)
+    ring()
+    torch.cuda.synchronize()
     diff = float((o_ring.float() - o_full.float()).abs().max() / o_full.float().abs().max())
     fl = 2.0 * h_t * dh * L * (L + 1)
-    log(f"[bench] ring attention: 4 CP ranks {ring_us:.1f} us (last rank {last_us:.1f} us) vs whole "
-        f"sequence {full_us:.1f} us, max_err {diff:.2e}")
+    log(f"[bench] ring attention: 4 CP ranks {ring_us:.1f} us as a graph (last rank {last_us:.1f} us; "
+        f"eager {eager_ring_us:.1f} us) vs whole sequence {full_us:.1f} us, max_err {diff:.2e}")
     if diff > 2e-2:
         log(f"[bench] PARITY FAILURE: ring attention differs from the whole-sequence core by {diff:.3e}")
     return {"what": "causal 8192-token sequence, 6 heads of 128, 4 context-parallel chunks of 2048: "
                     "all ranks' ring steps (init, 10 chunk folds, finish) vs one whole-sequence core call",
+            "timing": "graph replays; eager_ring_all_ranks_us: the same calls from the host",
             "ring_all_ranks_us": round(ring_us, 1), "whole_sequence_us": round(full_us, 1),
-            "last_rank_us": round(last_us, 1),
+            "last_rank_us": round(last_us, 1), "eager_ring_all_ranks_us": round(eager_ring_us, 1),
             "ring_tflops": round(fl / (ring_us * 1e-6) / 1e12, 1),
             "whole_tflops": round(fl / (full_us * 1e-6) / 1e12, 1),
             "max_err_vs_whole": diff}
