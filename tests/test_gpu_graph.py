@@ -1,7 +1,9 @@
 """The entry points allocate, free, synchronise and clear nothing themselves (every
 output is written by a kernel), so a caller can capture them in a HIP graph.  A forward
-step (two ranks' FFN shards and the partial sum with a residual) and a ring-attention
-pass (set-up, two chunk folds, finish) are captured once and replayed several times, with
+step (two ranks' FFN shards and the partial sum with a residual), an attention sublayer
+(two ranks' heads and out-projection shards, the sum with the residual) and a
+ring-attention pass (set-up, two chunk folds, finish) are captured once and replayed
+several times, with
 eager work and synchronisation between the replays; every replay must match the eager
 result bit for bit."""
 from __future__ import annotations
@@ -40,8 +42,9 @@ def _bits(t):
 @pytest.mark.parametrize("case", [(1000, 328, 1600, 2, "swiglu"), (2000, 5376, 6144, 2, "gelu")],
                          ids=["swiglu-small", "gelu-192-column-tiles"])
 def test_forward_step_graph_replays_match_eager(case):
-    """The second case runs the column GEMM on 128 x 192 tiles and the row GEMM on 256 x 192
-    tiles, both with the LDS-staged bf16 epilogue."""
+    """The second case runs the column GEMM split over k (fp32 partials in the workspace,
+    then the reduce kernel with GELU) on 256 x 192 tiles, and the row GEMM on 256 x 192
+    tiles with the LDS-staged bf16 epilogue."""
     T, d, d_ff, T_p, act = case
     log(f"[graph] forward step T={T} d={d} d_ff={d_ff} T_p={T_p} {act}")
     c = I.small_ffn_case(41, T, d, d_ff, act, I.BF16)
@@ -102,4 +105,43 @@ def test_ring_attention_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         for got, want in zip((o, st, lse), ref):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {i} differs"
+
+
+def test_attention_sublayer_graph_replays_match_eager():
+    """Two ranks' tp_attn_heads_shard_fwd (the Q, K, V projection split over k: fp32
+    partials in the workspace, then the reduce kernel; then the causal core) and
+    tp_attn_outproj_shard_fwd, and the sum of their partials with the residual."""
+    L, d, H, dh, T_p, ranks = 2048, 2048, 16, 128, 8, (0, 5)
+    kd = H // T_p * dh
+    log(f"[graph] attention sublayer L={L} d={d} H={H} T_p={T_p} ranks={ranks}")
+    g0 = np.random.default_rng(21)
+    x = dev(I.bf16_bits(g0.standard_normal((L, d)).astype(np.float32)), I.BF16)
+    wq, wk, wv = (dev(I.bf16_bits((g0.standard_normal((d, H * dh)) * 0.02).astype(np.float32)), I.BF16)
+                  for _ in range(3))
+    wo = dev(I.bf16_bits((g0.standard_normal((H * dh, d)) * 0.02).astype(np.float32)), I.BF16)
+    nb = S.tp_attn_heads_workspace_bytes(1, L, H, H, dh, T_p)
+    assert nb > L * 3 * kd * 2, "this shape should get split-K scratch"
+    ws = [torch.empty(nb, dtype=torch.uint8, device="cuda:0") for _ in ranks]
+    o = [torch.empty((L, kd), dtype=torch.bfloat16, device="cuda:0") for _ in ranks]
+    parts = torch.empty((len(ranks), L, d), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty((L, d), dtype=torch.bfloat16, device="cuda:0")
+
+    def sub():
+        for i, t in enumerate(ranks):
+            S.tp_attn_heads_shard_fwd(x, wq, wk, wv, o[i], ws[i], nb, 1, L, d, H, H, dh, T_p, t, True)
+            S.tp_attn_outproj_shard_fwd(o[i], wo, parts[i], L, d, H, H, dh, T_p, t, BF, BF)
+        S.tp_partial_sum(parts, L * d, len(ranks), x, y, L * d, BF, BF)
+
+    sub()
+    torch.cuda.synchronize()
+    ref = [y.clone(), parts.clone()] + [t.clone() for t in o]
+    g = _capture(sub)
+    for i in range(3):
+        for t in [y, parts] + o:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip([y, parts] + o, ref):
             assert torch.equal(_bits(got), _bits(want)), f"replay {i} differs"
