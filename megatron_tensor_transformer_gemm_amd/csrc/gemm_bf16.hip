@@ -474,6 +474,39 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   const int nk_all = LAYOUT == kNT ? nk0 + (g.K2 + BK - 1) / BK : (Kv + BK - 1) / BK;
   const int nk = (nk_all + NST - 1) / NST * NST;
 
+  // The backward's dH product (kNT with the activation's derivative): U (and V) come in and
+  // dU (and dV) go out through LDS as whole row segments, as the bf16 outputs do, instead
+  // of 8-byte accesses spread over 32 rows per instruction (its direct form cost ~430 us of
+  // a 70B rank's 5.0 ms backward).  Each wave stages its own WTM x WCOLS block of U in one
+  // region and of V in a second, where the whole set fits in the stage buffers.  With
+  // 64-row wave blocks the U (and V) row segments are loaded into registers before the
+  // k-loop (64 VGPRs at most), so that they arrive while the tile is multiplied instead of
+  // in a burst at every tile's end.
+  constexpr int DSREG = WTM * WCOLS * 2;
+  constexpr int DOPS = ACT == kActGelu ? 1 : 2;
+  constexpr bool DSTAGED = LAYOUT == kNT && ACT != kActNone && !OUT_F32 &&
+                           (WCOLS == 64 || WCOLS == 128) && STAGE % DSREG == 0 &&
+                           DOPS * NW * DSREG <= NST * STAGE;
+  constexpr int DSCH = WCOLS / 8, DSRPI = 64 / DSCH;   // chunks per row, rows per instruction
+  constexpr bool DPRE = DSTAGED && WTM == 64 && WCOLS == 64;
+  constexpr int NPRE = DPRE ? WTM / DSRPI : 1;
+  const bool dstaged = DSTAGED && (N_ & 7) == 0 && (g.ldu & 7) == 0;
+  bf16x8 pre_u[NPRE], pre_v[NPRE];
+  if constexpr (DPRE) {
+    if (dstaged) {
+#pragma unroll
+      for (int it = 0; it < NPRE; ++it) {
+        const int row = DSRPI * it + lane / DSCH, ch = lane % DSCH;
+        const int r = wm * WTM + row;
+        const int n = n0 + wn * WCOLS + ch * 8;
+        const bool in = r < rows_left && n < N_;
+        const int64_t off = (m0 + r) * g.ldu + n;
+        pre_u[it] = in ? *(const bf16x8*)((const __bf16*)g.U + off) : bf16x8{};
+        if constexpr (DOPS == 2) pre_v[it] = in ? *(const bf16x8*)((const __bf16*)g.V + off) : bf16x8{};
+      }
+    }
+  }
+
   // prologue: NST stages in flight, then stage 0's first fragments
 #pragma unroll
   for (int p = 0; p < NST; ++p) issue(p, buf(p));
@@ -578,6 +611,82 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   constexpr bool STAGED = !OUT_F32 && !SAVE && (ACT == kActNone || LAYOUT == kNN) &&
                           (POW2W ? STAGE % SREG == 0 && NW * SREG <= NST * STAGE
                                  : WCOLS == 96 && SPB >= 1 && NW <= NST * SPB);
+  if constexpr (DSTAGED) {
+    if (dstaged) {
+      constexpr int SCH = WCOLS / 8;        // 16-byte chunks per staged row
+      constexpr int SPITCH = WCOLS * 2;     // bytes per staged row
+      constexpr int SRPI = 64 / SCH;        // rows per load / store instruction
+      auto spos = [](int r, int c) -> int { return (c ^ r) & (SCH - 1); };
+      auto region = [&](int i) -> LDS_AS unsigned char* {
+        const int off = i * SREG;
+        return buf(off / STAGE) + off % STAGE;
+      };
+      LDS_AS unsigned char* RU = region(wave);
+      LDS_AS unsigned char* RV = region(DOPS == 2 ? NW + wave : wave);
+      __syncthreads();   // every wave's copies have landed and its fragment reads are done
+      // U [, V] of this wave's block -> LDS (zeros outside the matrix; never stored back)
+      if constexpr (DPRE) {
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it) {
+          const int row = SRPI * it + lane / SCH, ch = lane % SCH;
+          *(LDS_AS bf16x8*)(RU + row * SPITCH + (spos(row, ch) << 4)) = pre_u[it];
+          if constexpr (DOPS == 2) *(LDS_AS bf16x8*)(RV + row * SPITCH + (spos(row, ch) << 4)) = pre_v[it];
+        }
+      } else {
+#pragma unroll 4
+        for (int it = 0; it < WTM / SRPI; ++it) {
+          const int row = SRPI * it + lane / SCH, ch = lane % SCH;
+          const int r = wm * WTM + row;
+          const int n = n0 + wn * WCOLS + ch * 8;
+          const bool in = r < rows_left && n < N_;
+          const int64_t off = (m0 + r) * g.ldu + n;
+          const bf16x8 u = in ? *(const bf16x8*)((const __bf16*)g.U + off) : bf16x8{};
+          *(LDS_AS bf16x8*)(RU + row * SPITCH + (spos(row, ch) << 4)) = u;
+          if constexpr (DOPS == 2) {
+            const bf16x8 v = in ? *(const bf16x8*)((const __bf16*)g.V + off) : bf16x8{};
+            *(LDS_AS bf16x8*)(RV + row * SPITCH + (spos(row, ch) << 4)) = v;
+          }
+        }
+      }
+      __syncthreads();
+      // dU [, dV] from dH (the accumulators) at the same places, written back in place
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 32 + (lane & 31);
+#pragma unroll
+        for (int nb = 0; nb < NBS; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = nb * 32 + 8 * q + 4 * (lane >> 5);
+            const int pos = r * SPITCH + (spos(r, c >> 3) << 4) + (c & 7) * 2;
+            const bf16x4 uu = *(const LDS_AS bf16x4*)(RU + pos);
+            bf16x4 vv = bf16x4{};
+            if constexpr (DOPS == 2) vv = *(const LDS_AS bf16x4*)(RV + pos);
+            float du[4], dv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              act_backward<ACT>(acc[mb][nb][4 * q + e], (float)uu[e], (float)vv[e], du[e], dv[e]);
+            *(LDS_AS bf16x4*)(RU + pos) = bf16x4{(__bf16)du[0], (__bf16)du[1], (__bf16)du[2], (__bf16)du[3]};
+            if constexpr (DOPS == 2)
+              *(LDS_AS bf16x4*)(RV + pos) = bf16x4{(__bf16)dv[0], (__bf16)dv[1], (__bf16)dv[2], (__bf16)dv[3]};
+          }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < WTM / SRPI; ++it) {
+        const int row = SRPI * it + lane / SCH, ch = lane % SCH;
+        const int r = wm * WTM + row;
+        const int n = n0 + wn * WCOLS + ch * 8;
+        if (r < rows_left && n < N_) {
+          const int64_t off = (m0 + r) * ldc_ + n;
+          *(bf16x8*)((__bf16*)Cseg + off) = *(const LDS_AS bf16x8*)(RU + row * SPITCH + (spos(row, ch) << 4));
+          if constexpr (DOPS == 2)
+            *(bf16x8*)((__bf16*)g.dV + off) = *(const LDS_AS bf16x8*)(RV + row * SPITCH + (spos(row, ch) << 4));
+        }
+      }
+      return;
+    }
+  }
   if constexpr (STAGED) {
     if ((N_ & 7) == 0) {
       constexpr int SCH = WCOLS / 8;        // 16-byte chunks per staged row
