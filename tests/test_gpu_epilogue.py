@@ -106,12 +106,17 @@ def test_forward_epilogue_elementwise(act, shape):
 
 
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
-@pytest.mark.parametrize("shape", [(1000, 256, 2, None), (4100, 1032, 2, 1)],
-                         ids=["small-tiles-both-ranks", "large-tiles-rank1"])
+@pytest.mark.parametrize("shape", [(1000, 256, 2, None), (4100, 1032, 2, 1), (4160, 4096, 1, 0),
+                                   (4096, 4096, 1, 0)],
+                         ids=["small-tiles-both-ranks", "large-tiles-rank1", "128x256-tiles",
+                              "256x256-tiles"])
 def test_backward_epilogue_elementwise(act, shape):
     """tp_ffn_shard_bwd's dU (and dV), which it leaves in its workspace: dH = dY W2(t)^T
     is exactly dy[:, :n], so every element is the derivative formula at the saved bf16
-    U, V times an exact dH; within one bf16 step of the oracle's act_backward."""
+    U, V times an exact dH; within one bf16 step of the oracle's act_backward.  The dH
+    product's tiles: 128 x 128 (first two shapes) and 128 x 256 (8 waves; U, V loaded
+    before the k-loop) stage the epilogue through LDS; 256 x 256 stages it for GELU and
+    keeps direct accesses for SwiGLU (U and V of all waves do not fit in LDS)."""
     T, n, T_p, only = shape
     d, d_ff = 2 * n, T_p * n
     log(f"[epilogue-bwd] act={act} T={T} n={n} T_p={T_p}")
