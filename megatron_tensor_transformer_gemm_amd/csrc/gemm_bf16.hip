@@ -36,6 +36,7 @@
 //    so concurrently running tiles of one XCD share A and B panels in its L2.
 #include "tp_internal.h"
 #include "lds_copy.h"
+#include <atomic>
 
 namespace tpk {
 namespace {
@@ -826,6 +827,385 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   }
 }
 
+// ---- Forward products of more than one wave of 256 x 256 tiles: one workgroup per CU
+// takes tiles gridDim.x apart, and the copy pipeline runs on across tile boundaries.  The
+// second-to-last stage of a tile copies k-tile 0 of the workgroup's next tile (instead of
+// the zero fill that pads a lone tile's loop); the last stage copies nothing, so that
+// k-tile 0 arrives while the last stages multiply and the epilogue runs, and is waited
+// for after it (with k-tile 1 issued then).  The epilogue therefore may not use the stage
+// buffers: each wave rounds its 128-row block 32 rows at a time into a 4 KiB region of
+// its own (32 KiB beside the two 64 KiB stages: the whole 160 KiB of LDS) and stores
+// whole row segments from there, with no workgroup barrier.
+// A workgroup launched per tile cost 4-5 us per tile that this hides (probe timestamps in
+// the 70B products: dispatch gap 0.8-1.3 us, prologue 1.9-2.5 us, store drain 0.4-0.8 us).
+// Copies, fragment reads and MFMA order are those of gemm_bf16_kernel in the forward layout
+// with 256 x 256 x 64 tiles, two stages and 8 waves, so the results are bit-identical.
+template <bool DUAL, int ACT>
+__global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256, BK = 64, NST = 2, NW = 8;
+  constexpr int NSUB = DUAL ? 2 : 1;          // B sub-tiles: W1 block | W3 block
+  constexpr int BNS = BN / NSUB;              // output columns per tile
+  constexpr int WNG = 4;                      // waves along N (2 x 4)
+  constexpr int WTM = BM / (NW / WNG);        // 128 rows per wave
+  constexpr int MB = WTM / 32;
+  constexpr int WCOLS = BNS / WNG;            // 32 (gated pair) or 64 columns per wave
+  constexpr int NBS = WCOLS / 32;
+  constexpr int NB = NBS * NSUB;
+  constexpr int KSUB = BK / 16;
+  constexpr int ACPR = BK / 8;
+  constexpr int AROWB = BK * 2;
+  constexpr int ARPI = 1024 / AROWB;
+  constexpr int A_BYTES = BM * AROWB;
+  constexpr int SUB_BYTES = BK * BNS * 2;
+  constexpr int STAGE = A_BYTES + NSUB * SUB_BYTES;
+  constexpr int A_LD = A_BYTES / 1024 / NW;
+  constexpr int B_LD = NSUB * SUB_BYTES / 1024 / NW;
+  constexpr int LPS = A_LD + B_LD;
+  constexpr int QSUB = SUB_BYTES / 1024;
+  constexpr int CPR = BNS / 8;
+  constexpr int PITCH = BNS * 2;
+  constexpr int ECH = WCOLS / 8;              // 16-byte chunks per staged row
+  constexpr int EPITCH = WCOLS * 2;           // bytes per staged row
+  constexpr int ERPI = 64 / ECH;              // staged rows per store instruction
+  constexpr int EREG = 4096;                  // one wave's staging region
+  static_assert(STAGE == 65536 && LPS == 8 && 32 * EPITCH <= EREG, "tile shape");
+  static_assert(2 * STAGE + NW * EREG <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ep[NW * EREG];
+  auto buf = [&](int i) -> LDS_AS unsigned char* {
+    return i == 0 ? (LDS_AS unsigned char*)st0 : (LDS_AS unsigned char*)st1;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WNG, wn = wave % WNG;
+  const int64_t ntile = (int64_t)tiles_m * tiles_n;
+  const int nk = ((g.K + BK - 1) / BK + NST - 1) / NST * NST;   // k-tiles, padded
+
+  // ---- the tile whose stages are being copied.  The k of a lane's A chunk and its B
+  // k-row do not depend on the tile; the offsets do (masks, segment strides).
+  int a_kc[A_LD], b_kr[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int row = (wave * A_LD + i) * ARPI + lane / ACPR;
+    a_kc[i] = 8 * ((lane % ACPR) ^ swz_a<ACPR>(row));
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) b_kr[i] = (((wave * B_LD + i) % QSUB) * 64 + lane) / CPR;
+  const bool b_second = (wave * B_LD) / QSUB != 0;
+  uint32_t a_voff[A_LD], b_voff[B_LD];
+  const __bf16* A = nullptr;
+  const __bf16* Bc = nullptr;                 // this wave's B sub-tile
+  __bf16* Cseg = nullptr;
+  int64_t m0 = 0;
+  int n0 = 0, rows_left = 0, N_ = 0, ldb_ = 0, ldc_ = 0;
+  // has_tile false: every copy out of range (zero fill, no memory traffic)
+  auto set_tile = [&](int64_t tile, bool has_tile) {
+    int tm = 0, tn = 0;
+    if (has_tile) map_tile((int)tile, tiles_m, tiles_n, tm, tn);
+    const void* Bseg = g.B0;
+    void* Cs = g.C;
+    int Nn = g.N, ldb = g.ldb, ldc = g.ldc;
+    if (!DUAL && g.nseg > 1) {
+      const int t0 = (g.N + BNS - 1) / BNS;
+      if (tn >= t0) {
+        tn -= t0;
+        const int t1 = (g.Nx[0] + BNS - 1) / BNS;
+        const int sg = (g.nseg > 2 && tn >= t1) ? 1 : 0;
+        if (sg) tn -= t1;
+        Bseg = g.Bx[sg];
+        Cs = g.Cx[sg];
+        Nn = g.Nx[sg];
+        ldb = g.ldbx[sg];
+        ldc = g.ldcx[sg];
+      }
+    }
+    m0 = (int64_t)tm * BM;
+    n0 = tn * BNS;
+    const int64_t rl = g.M - m0;
+    rows_left = has_tile ? (rl < BM ? (int)rl : BM) : 0;
+    N_ = Nn;
+    ldb_ = ldb;
+    ldc_ = ldc;
+    Cseg = (__bf16*)Cs;
+    A = (const __bf16*)g.A + m0 * g.lda;
+    Bc = (const __bf16*)(DUAL && b_second ? g.B1 : Bseg) + n0;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int row = (wave * A_LD + i) * ARPI + lane / ACPR;
+      a_voff[i] = row < rows_left ? (uint32_t)(row * g.lda + a_kc[i]) * 2u : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int pos = ((wave * B_LD + i) % QSUB) * 64 + lane;
+      const int c = (pos % CPR) ^ (swz_b(b_kr[i]) & (CPR - 1));
+      b_voff[i] = (has_tile && n0 + 8 * c < N_) ? (uint32_t)(b_kr[i] * ldb_ + 8 * c) * 2u : kOOB;
+    }
+  };
+
+  // Copies [first, first + count) of k-tile kt of the tile set_tile chose.
+  auto issue_range = [&](int kt, LDS_AS unsigned char* base, int first, int count) {
+    const int k0 = kt * BK;
+    const bool full = k0 + BK <= g.K;
+    const i32x4 da = make_desc(A + k0);
+    const i32x4 db = make_desc(Bc + (int64_t)k0 * ldb_);
+    const uint32_t lds = (uint32_t)(uintptr_t)base;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      if (i < first || i >= first + count) continue;
+      const uint32_t v = (full || k0 + a_kc[i] < g.K) ? a_voff[i] : kOOB;
+      copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (wave * A_LD + i) * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      if (A_LD + i < first || A_LD + i >= first + count) continue;
+      const uint32_t v = (full || k0 + b_kr[i] < g.K) ? b_voff[i] : kOOB;
+      copy16_to_lds(db, v, __builtin_amdgcn_readfirstlane(lds + A_BYTES + (wave * B_LD + i) * 1024));
+    }
+  };
+
+  // ---- per-lane LDS read offsets (as gemm_bf16_kernel)
+  const int arow = wm * WTM + (lane & 31);
+  uint32_t a_rd[KSUB];
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s) {
+    const int c = 2 * s + (lane >> 5);
+    a_rd[s] = (uint32_t)(arow * AROWB + ((c ^ swz_a<ACPR>(arow)) << 4));
+  }
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const int krow_l = 8 * (g4 >> 1) + (i16 >> 2);
+  const int sw = swz_b(krow_l) & (CPR - 1);
+  uint32_t b_rd[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int sub = nb / NBS;
+    const int colbase = wn * WCOLS + (nb % NBS) * 32;
+    const int n = colbase + 16 * (g4 & 1) + 4 * (i16 & 3);
+    b_rd[nb] = (uint32_t)(sub * SUB_BYTES + krow_l * PITCH + (((n >> 3) ^ sw) << 4) + ((n >> 2) & 1) * 8);
+  }
+
+  f32x16 acc[MB][NB];
+  bf16x8 af[2][MB];
+  bf16x8 bfr[2][NB];
+  auto load_frags = [&](const LDS_AS unsigned char* As, int s, bf16x8 (&a)[MB], bf16x8 (&b)[NB]) {
+    const LDS_AS unsigned char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *(const LDS_AS bf16x8*)(As + a_rd[s] + mb * 32 * AROWB);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const LDS_AS unsigned char* p = Bs + b_rd[nb] + 16 * s * PITCH;
+      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+      b[nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto read_group = [&](const LDS_AS unsigned char* As, int j) {
+    if (j < MB) {
+      af[0][j] = *(const LDS_AS bf16x8*)(As + a_rd[0] + j * 32 * AROWB);
+    } else {
+      const int nb = j - MB;
+      const LDS_AS unsigned char* p = As + A_BYTES + b_rd[nb];
+      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+      bfr[0][nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb], a[mb], acc[mb][nb], 0, 0, 0);
+  };
+  constexpr int NREAD = MB + 2 * NB;
+  constexpr int NMFMA = MB * NB;
+  constexpr int NPAIR = NMFMA < NREAD ? NMFMA : NREAD;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
+    if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
+  };
+
+  // Epilogue target of the tile being multiplied (set_tile moves on to the next tile
+  // before the last stages' copies)
+  __bf16* e_c = nullptr;
+  int64_t e_m0 = 0;
+  int e_n0 = 0, e_rows = 0, e_N = 0, e_ldc = 0;
+  int64_t tile = blockIdx.x;
+  bool next_ok = false;
+
+  // One stage of the tile (all but the last); at stage nk - NST the copies move on to
+  // the next tile.
+  auto stage = [&](int kt, int u) {
+    LDS_AS unsigned char* cur = buf(u);
+    LDS_AS unsigned char* nxt = buf(u + 1 == NST ? 0 : u + 1);
+#pragma unroll
+    for (int s = 0; s + 1 < KSUB; ++s) {
+      load_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+      mfmas(af[s & 1], bfr[s & 1]);
+      interleave();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // k-tile kt+1 (of this tile or the next) is complete for every wave; this stage's
+    // buffer is free for k-tile kt+NST
+    sync_copies<(NST - 2) * LPS>();
+    if (kt == nk - NST) {
+      e_c = Cseg;
+      e_m0 = m0;
+      e_n0 = n0;
+      e_rows = rows_left;
+      e_N = N_;
+      e_ldc = ldc_;
+      next_ok = tile + gridDim.x < ntile;
+      set_tile(tile + gridDim.x, next_ok);
+    }
+    const int kc = kt + NST < nk ? kt + NST : kt + NST - nk;
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NFR = MB + NB;
+    constexpr int NITEM = LPS + NFR;
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+      const int mb = i / NB, nb = i % NB;
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][nb], af[1][mb], acc[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NITEM; ++j) {
+        if (j * NMFMA / NITEM != i) continue;
+        if (j < LPS) issue_range(kc, cur, j, 1);
+        else read_group(nxt, j - LPS);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Products without an activation (partial sums read later by the partial-sum kernel)
+  // are stored non-temporally, as in gemm_bf16_kernel.  (Every output segment is a
+  // multiple of 8 columns wide with 16-byte aligned rows: the launcher checks.)
+  auto store_out = [](const bf16x8& v, bf16x8* dst) {
+    if constexpr (ACT == kActNone) __builtin_nontemporal_store(v, dst);
+    else *dst = v;
+  };
+  // physical chunk of chunk c in staged row r (as gemm_bf16_kernel's staging)
+  auto spos = [](int r, int c) -> int {
+    if constexpr (ECH == 4) return (c ^ (r >> 2)) & 3;
+    else return (c ^ r) & (ECH - 1);
+  };
+  LDS_AS unsigned char* E = (LDS_AS unsigned char*)ep + wave * EREG;
+
+  // ---- first tile: prologue
+  set_tile(tile, true);
+#pragma unroll
+  for (int p = 0; p < NST; ++p) issue_range(p, buf(p), 0, LPS);
+  sync_copies<(NST - 1) * LPS>();
+  load_frags(buf(0), 0, af[0], bfr[0]);
+
+  static_assert(NST == 2, "the tile transition below assumes two stages");
+  for (;;) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+    for (int kt0 = 0; kt0 + NST < nk; kt0 += NST) {
+#pragma unroll
+      for (int u = 0; u < NST; ++u) stage(kt0 + u, u);
+    }
+    stage(nk - 2, 0);   // copies k-tile 0 of the next tile
+    // The last stage: no copies and no reads of the next stage, so that the next tile's
+    // k-tile 0 (copied since stage nk - 2) is waited for only after the epilogue.
+    {
+      const LDS_AS unsigned char* cur = buf(1);
+#pragma unroll
+      for (int s = 0; s + 1 < KSUB; ++s) {
+        load_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+        mfmas(af[s & 1], bfr[s & 1]);
+        interleave();
+      }
+      mfmas(af[1], bfr[1]);
+    }
+    // ---- epilogue: 32 rows at a time through this wave's own region; the next tile's
+    // first stages are in flight meanwhile.  (The lane index goes through an empty asm so
+    // that the epilogue's per-lane offsets are formed here rather than hoisted out of the
+    // tile loop, where they would hold registers through every k-loop.)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = ln & 31;
+#pragma unroll
+      for (int nb = 0; nb < NBS; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = nb * 32 + 8 * q + 4 * (ln >> 5);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = epilogue<ACT>(acc[mb][nb][4 * q + e], DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f);
+          *(LDS_AS bf16x4*)(E + r * EPITCH + (spos(r, c >> 3) << 4) + (c & 7) * 2) =
+              bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        }
+#pragma unroll
+      for (int it = 0; it < 32 / ERPI; ++it) {
+        const int row = ERPI * it + ln / ECH, ch = ln % ECH;
+        const bf16x8 v = *(const LDS_AS bf16x8*)(E + row * EPITCH + (spos(row, ch) << 4));
+        const int rr = wm * WTM + mb * 32 + row;
+        const int n = e_n0 + wn * WCOLS + ch * 8;
+        if (rr < e_rows && n < e_N) store_out(v, (bf16x8*)(e_c + (e_m0 + rr) * e_ldc + n));
+      }
+    }
+    if (!next_ok) break;
+    tile += gridDim.x;
+    // the next tile's k-tile 1 into buffer 1 once every wave has read it; then k-tile 0
+    // complete for every wave (the loads land in order, pending stores only lengthen it)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue_range(1, buf(1), 0, LPS);
+    sync_copies<LPS>();
+    load_frags(buf(0), 0, af[0], bfr[0]);
+  }
+  // the trailing zero-fill copies must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// A bf16 forward product with more tiles of 256 x 256 than the GPU has CUs runs on the
+// persistent kernel, one workgroup per CU; false when it does not apply.
+template <bool DUAL, int ACT>
+bool launch_persistent(const GemmDesc& g, hipStream_t s, hipError_t& e) {
+  constexpr int OUT_BN = DUAL ? 128 : 256;
+  const int64_t tm = (g.M + 255) / 256;
+  int64_t tn = (g.N + OUT_BN - 1) / OUT_BN;
+  for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) tn += (g.Nx[i] + OUT_BN - 1) / OUT_BN;
+  const int cus = device_cus();
+  if (g.ksplit > 1 || cus <= 0 || tm * tn <= cus || tm * tn > 0x7FFFFFFF) return false;
+  // the epilogue stores 16-byte row segments
+  bool rows16 = g.N % 8 == 0 && g.ldc % 8 == 0;
+  for (int i = 0; i + 1 < g.nseg && !DUAL; ++i) rows16 = rows16 && g.Nx[i] % 8 == 0 && g.ldcx[i] % 8 == 0;
+  if (!rows16) return false;
+  hipLaunchKernelGGL((gemm_fwd_persistent_kernel<DUAL, ACT>), dim3((unsigned)cus), dim3(512), 0, s, g,
+                     (int)tm, (int)tn);
+  e = hipGetLastError();
+  return true;
+}
+
 template <int BM, int BN, int BK, int NST, bool DUAL, int ACT, bool OUT_F32, int LAYOUT, bool SAVE, int NW = 4>
 hipError_t launch_cfg(const GemmDesc& g, hipStream_t s) {
   constexpr int OUT_BN = DUAL ? BN / 2 : BN;
@@ -1036,6 +1416,10 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     // when those occupy half of them; 128x128 only below that.
     if (big >= 192) {
       if constexpr (!SAVE) {
+        if constexpr (!OUT_F32) {
+          hipError_t e;
+          if (launch_persistent<DUAL, ACT>(g, s, e)) return e;
+        }
         return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
       } else {
         if (kdepth > 2048) return launch_cfg<256, 256, 32, 4, DUAL, ACT, OUT_F32, LAYOUT, SAVE>(g, s);
@@ -1067,6 +1451,10 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
     // 32-deep stages: 70B column GEMM + SwiGLU 1,440 against 1,470 us, row GEMM 735-748
     // against 754 us, out-projection 257-261 against 273 us (two 64-deep stages).
     if constexpr (LAYOUT == kNN && !SAVE) {
+      if constexpr (!OUT_F32) {
+        hipError_t e;
+        if (launch_persistent<DUAL, ACT>(g, s, e)) return e;
+      }
       return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
     } else if constexpr (LAYOUT == kTN) {
       // the weight gradients: 8 waves with four 32-deep stages (two 64-deep ones measured

@@ -41,6 +41,9 @@ CASES = [
     (3, 64, 128, 4, 2, 128, 1, True),
     (1, 130, 192, 8, 8, 128, 4, False),
     (2, 1, 64, 2, 2, 64, 1, True),
+    # fused Q, K, V product of 64 x 6 tiles, more than the GPU's CUs: one workgroup per CU
+    # over several tiles, crossing the three column segments
+    (8, 2048, 512, 16, 2, 128, 2, True),
 ]
 
 

@@ -52,6 +52,29 @@ def test_integer_offsets_bit_exact(act, shape):
         assert np.array_equal(host64(y), y_ref), f"y({t}) differs"
 
 
+@pytest.mark.parametrize("act,shape", [("none", (4100, 4104, 2, 4104)), ("bilinear", (4100, 4104, 2, 2200))],
+                         ids=["none-289-tiles", "bilinear-306-tiles"])
+def test_integer_persistent_bit_exact(act, shape):
+    """More 256 x 256 tiles than the GPU has CUs (289 and 306 here): the column and row
+    products run one workgroup per CU over several tiles each, with ragged M, N and K.
+    Integer inputs, bf16 outputs: H(t) equals the oracle bit for bit, and y(t) equals the
+    oracle's exact integer sum rounded once to bf16 (round to nearest, ties to even)."""
+    T, d, T_p, n = shape
+    d_ff = T_p * n
+    t = 1
+    log(f"[integer persistent] act={act} T={T} d={d} d_ff={d_ff} T_p={T_p} t={t}")
+    c = I.integer_offset_case(T, d, d_ff, seed=11)
+    xd, w1d, w3d, w2d = (dev(c[k], I.BF16) for k in ("x", "w1", "w3", "w2"))
+    x, w1, w3, w2 = (f64(c[k], I.BF16) for k in ("x", "w1", "w3", "w2"))
+    y, h = _run_shard(xd, w1d, w3d if act == "bilinear" else None, w2d, T, d, d_ff, T_p, t,
+                      act, S.TP_BF16, S.TP_BF16)
+    h_ref, y_ref = O.ffn_shard(x, w1, w3, w2, T_p, t, act)
+    assert np.abs(y_ref).max() < 2 ** 24
+    assert np.array_equal(host64(h), h_ref), "H(t) differs"
+    y_ref_bf16 = f64(I.bf16_bits(y_ref.astype(np.float32)), I.BF16)
+    assert np.array_equal(host64(y), y_ref_bf16), "y(t) differs"
+
+
 # ----------------------------------------------------------------------------- float parity
 CASES = [
     # T, d, d_ff, T_p, act, in, out
