@@ -11,7 +11,9 @@
 // element-wise, so the sharded hidden state needs no communication).
 //
 // Design (one workgroup per output tile: 8 waves, two per SIMD, so that one wave of a
-// SIMD multiplies while the other issues copies; small-tile fallbacks keep 4 waves):
+// SIMD multiplies while the other issues copies; small-tile fallbacks keep 4 waves.
+// Forward products of more tiles than CUs run a persistent form: one workgroup per CU
+// walks its tiles with the copy pipeline running on across tile boundaries):
 //  * HBM/L2 -> LDS with buffer_load ... lds (16 B per lane): no staging VGPRs,
 //    out-of-range rows/columns/k come back as zeros from the buffer
 //    descriptor's range check (masked lanes get an out-of-range offset), so
