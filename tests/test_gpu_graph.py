@@ -39,12 +39,15 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("case", [(1000, 328, 1600, 2, "swiglu"), (2000, 5376, 6144, 2, "gelu")],
-                         ids=["swiglu-small", "gelu-192-column-tiles"])
+@pytest.mark.parametrize("case", [(1000, 328, 1600, 2, "swiglu"), (2000, 5376, 6144, 2, "gelu"),
+                                  (4100, 4104, 8208, 2, "swiglu")],
+                         ids=["swiglu-small", "gelu-192-column-tiles", "swiglu-persistent"])
 def test_forward_step_graph_replays_match_eager(case):
     """The second case runs the column GEMM split over k (fp32 partials in the workspace,
     then the reduce kernel with GELU) on 256 x 192 tiles, and the row GEMM on 256 x 192
-    tiles with the LDS-staged bf16 epilogue."""
+    tiles with the LDS-staged bf16 epilogue.  The third has more 256 x 256 tiles than the
+    GPU has CUs in both products (561 and 289): both run one workgroup per CU over several
+    tiles each."""
     T, d, d_ff, T_p, act = case
     log(f"[graph] forward step T={T} d={d} d_ff={d_ff} T_p={T_p} {act}")
     c = I.small_ffn_case(41, T, d, d_ff, act, I.BF16)
