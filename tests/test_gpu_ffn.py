@@ -52,16 +52,22 @@ def test_integer_offsets_bit_exact(act, shape):
         assert np.array_equal(host64(y), y_ref), f"y({t}) differs"
 
 
-@pytest.mark.parametrize("act,shape", [("none", (4100, 4104, 2, 4104)), ("bilinear", (4100, 4104, 2, 2200))],
-                         ids=["none-289-tiles", "bilinear-306-tiles"])
+@pytest.mark.parametrize("act,shape", [("none", (4100, 4104, 2, 4104)), ("bilinear", (4100, 4104, 2, 2200)),
+                                       ("none", (16384, 64, 2, 1280)), ("bilinear", (16384, 8, 2, 640)),
+                                       ("none", (65792, 256, 1, 8))],
+                         ids=["none-289-tiles", "bilinear-306-tiles", "k64-two-stage-loop",
+                              "k8-one-ragged-k-tile", "257-tiles"])
 def test_integer_persistent_bit_exact(act, shape):
-    """More 256 x 256 tiles than the GPU has CUs (289 and 306 here): the column and row
-    products run one workgroup per CU over several tiles each, with ragged M, N and K.
-    Integer inputs, bf16 outputs: H(t) equals the oracle bit for bit, and y(t) equals the
-    oracle's exact integer sum rounded once to bf16 (round to nearest, ties to even)."""
+    """More 256 x 256 tiles than the GPU has CUs: the products run one workgroup per CU over
+    several tiles each.  289 and 306 tiles with ragged M, N and K; column products whose
+    k-loop is two stages long (k 64), so the copies move on to the next tile at the first
+    stage, or one ragged k-tile (k 8); and 257 tiles in both products, one workgroup taking
+    a second.  Integer inputs, bf16 outputs: H(t) equals the oracle bit for bit, and y(t)
+    equals the oracle's exact integer sum rounded once to bf16 (round to nearest, ties to
+    even)."""
     T, d, T_p, n = shape
     d_ff = T_p * n
-    t = 1
+    t = min(1, T_p - 1)
     log(f"[integer persistent] act={act} T={T} d={d} d_ff={d_ff} T_p={T_p} t={t}")
     c = I.integer_offset_case(T, d, d_ff, seed=11)
     xd, w1d, w3d, w2d = (dev(c[k], I.BF16) for k in ("x", "w1", "w3", "w2"))
