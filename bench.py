@@ -607,6 +607,19 @@ def measure_backward(w, X, W1, W3, W2, steps: int, warmup: int) -> dict:
         h, u, v = (torch.empty((T, n), dtype=torch.bfloat16, device="cuda") for _ in range(3))
         S.tp_ffn_shard_fwd_train(X, W1, W3, W2, yt, h, u, v, T, d, d_ff, T_p, t, S.TP_ACT_SWIGLU, BF)
         saved.append((h, u, v))
+    # the training forward itself (it keeps H, U, V): every rank's call between events,
+    # after one untimed pass
+    fwd_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(2 * T_p)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(fwd_ev):
+        t = i % T_p
+        h, u, v = saved[t]
+        e0.record()
+        S.tp_ffn_shard_fwd_train(X, W1, W3, W2, yt, h, u, v, T, d, d_ff, T_p, t, S.TP_ACT_SWIGLU, BF)
+        e1.record()
+    torch.cuda.synchronize()
+    fwd_us = 1e3 * sum(a.elapsed_time(b) for a, b in fwd_ev) / len(fwd_ev)
     del yt
     dW1 = torch.empty((d, d_ff), dtype=torch.float32, device="cuda")
     dW3 = torch.empty((d, d_ff), dtype=torch.float32, device="cuda")
@@ -653,8 +666,14 @@ def measure_backward(w, X, W1, W3, W2, steps: int, warmup: int) -> dict:
            "flops_per_rank": fl_rank,
            "dx_partial_sum_us": round(psum_us, 1),
            "dtypes": {"inputs": "bf16", "dx": "bf16", "weight_grads": "f32"},
-           "steps": steps}
-    log(f"[bench] backward: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; per rank {rank_us:.1f} us")
+           "steps": steps,
+           "train_forward": {"what": "tp_ffn_shard_fwd_train of one rank: the forward shard that "
+                                     "also keeps H, U, V for the backward",
+                             "per_rank_us": round(fwd_us, 1),
+                             "tflops": round(6.0 * T * d * n / (fwd_us * 1e-6) / 1e12, 1),
+                             "calls": len(fwd_ev)}}
+    log(f"[bench] backward: {ms:.3f} ms/step, {res['tflops']} TFLOP/s; per rank {rank_us:.1f} us; "
+        f"training forward per rank {fwd_us:.1f} us")
     return res
 
 

@@ -612,7 +612,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   // (32-column blocks: the gated pair's 128 output columns over 4 waves)
   constexpr bool POW2W = WCOLS == 32 || WCOLS == 64 || WCOLS == 128;
   constexpr int SPB = STAGE / SREG;       // wave regions per stage buffer (96-column blocks)
-  constexpr bool STAGED = !OUT_F32 && !SAVE && (ACT == kActNone || LAYOUT == kNN) &&
+  // The training forward (SAVE) stages H, then U, then V through the same wave region
+  // (8-wave tiles; the 4-wave ones have no registers to spare for it).
+  constexpr bool STAGED = !OUT_F32 && (!SAVE || (LAYOUT == kNN && POW2W && NW == 8)) &&
+                          (ACT == kActNone || LAYOUT == kNN) &&
                           (POW2W ? STAGE % SREG == 0 && NW * SREG <= NST * STAGE
                                  : WCOLS == 96 && SPB >= 1 && NW <= NST * SPB);
   if constexpr (DSTAGED) {
@@ -696,7 +699,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     }
   }
   if constexpr (STAGED) {
-    if ((N_ & 7) == 0) {
+    if ((N_ & 7) == 0 && (!SAVE || (g.ldu & 7) == 0)) {
       constexpr int SCH = WCOLS / 8;        // 16-byte chunks per staged row
       constexpr int SPITCH = WCOLS * 2;     // bytes per staged row
       // physical chunk of chunk c in staged row r
@@ -725,46 +728,55 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
       } else {
         R = buf(wave / SPB) + (wave % SPB) * SREG;
       }
+      // one pass per output: H (activated); with SAVE also U and V (pre-activations)
+      constexpr int NPASS = SAVE ? (DUAL ? 3 : 2) : 1;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = mb * 32 + (lane & 31);
+      for (int pass = 0; pass < NPASS; ++pass) {
 #pragma unroll
-        for (int nb = 0; nb < NBS; ++nb)
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = mb * 32 + (lane & 31);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = nb * 32 + 8 * q + 4 * (lane >> 5);
-            float v[4];
+          for (int nb = 0; nb < NBS; ++nb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float u = acc[mb][nb][4 * q + e];
-              if constexpr (LAYOUT == kNN) v[e] = epilogue<ACT>(u, DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f);
-              else v[e] = u;
+            for (int q = 0; q < 4; ++q) {
+              const int c = nb * 32 + 8 * q + 4 * (lane >> 5);
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float u = acc[mb][nb][4 * q + e];
+                if (pass == 1) v[e] = u;
+                else if (pass == 2) v[e] = acc[mb][nb + NBS][4 * q + e];
+                else if constexpr (LAYOUT == kNN) v[e] = epilogue<ACT>(u, DUAL ? acc[mb][nb + NBS][4 * q + e] : 0.0f);
+                else v[e] = u;
+              }
+              *(LDS_AS bf16x4*)(R + r * SPITCH + (spos(r, c >> 3) << 4) + (c & 7) * 2) =
+                  bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
             }
-            *(LDS_AS bf16x4*)(R + r * SPITCH + (spos(r, c >> 3) << 4) + (c & 7) * 2) =
-                bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          }
-      }
-      __syncthreads();
-      if constexpr (POW2W) {
-        constexpr int SRPI = 64 / SCH;      // rows per store instruction
-#pragma unroll 4
-        for (int it = 0; it < WTM / SRPI; ++it) {
-          const int row = SRPI * it + lane / SCH, ch = lane % SCH;
-          const int r = wm * WTM + row;
-          const int n = n0 + wn * WCOLS + ch * 8;
-          const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
-          if (r < rows_left && n < N_) store_out(v, (bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n));
         }
-      } else {
-        static_assert((WTM * SCH) % 64 == 0, "whole store instructions");
+        if (pass == 0) __syncthreads();
+        if constexpr (POW2W) {
+          constexpr int SRPI = 64 / SCH;      // rows per store instruction
+          __bf16* dst = pass == 0 ? (__bf16*)Cseg : (__bf16*)(pass == 1 ? g.U : g.V);
+          const int64_t ld = pass == 0 ? ldc_ : g.ldu;
 #pragma unroll 4
-        for (int it = 0; it < WTM * SCH / 64; ++it) {
-          const int idx = it * 64 + lane;
-          const int row = idx / SCH, ch = idx % SCH;
-          const int r = wm * WTM + row;
-          const int n = n0 + wn * WCOLS + ch * 8;
-          const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
-          if (r < rows_left && n < N_) store_out(v, (bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n));
+          for (int it = 0; it < WTM / SRPI; ++it) {
+            const int row = SRPI * it + lane / SCH, ch = lane % SCH;
+            const int r = wm * WTM + row;
+            const int n = n0 + wn * WCOLS + ch * 8;
+            const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
+            if (r < rows_left && n < N_) store_out(v, (bf16x8*)(dst + (m0 + r) * ld + n));
+          }
+        } else {
+          static_assert((WTM * SCH) % 64 == 0, "whole store instructions");
+#pragma unroll 4
+          for (int it = 0; it < WTM * SCH / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int row = idx / SCH, ch = idx % SCH;
+            const int r = wm * WTM + row;
+            const int n = n0 + wn * WCOLS + ch * 8;
+            const bf16x8 v = *(const LDS_AS bf16x8*)(R + row * SPITCH + (spos(row, ch) << 4));
+            if (r < rows_left && n < N_) store_out(v, (bf16x8*)((__bf16*)Cseg + (m0 + r) * ldc_ + n));
+          }
         }
       }
       return;

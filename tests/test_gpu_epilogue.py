@@ -63,8 +63,9 @@ SHAPE_IDS = ["small-tiles-both-ranks", "256x256-tiles-rank1"]
 @pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
 def test_forward_epilogue_elementwise(act, shape):
     """tp_ffn_shard_fwd (H staged through LDS, then row segments stored) and
-    tp_ffn_shard_fwd_train (H, U, V stored from the registers): every H element within
-    one bf16 step of the oracle; U, V equal the chosen pre-activations; y(t) = [H | 0]."""
+    tp_ffn_shard_fwd_train (H, U, V stored from the registers on small tiles, staged through
+    LDS one after another on 8-wave 256 x 256 tiles): every H element within one bf16 step
+    of the oracle; U, V equal the chosen pre-activations; y(t) = [H | 0]."""
     T, n, T_p, only = shape
     d, d_ff = 2 * n, T_p * n
     log(f"[epilogue-fwd] act={act} T={T} n={n} T_p={T_p}")
@@ -91,7 +92,7 @@ def test_forward_epilogue_elementwise(act, shape):
         S.tp_ffn_shard_fwd_train(dd["x"], dd["w1"], w3d, dd["w2"], yt, h2, u2, v2, T, d, d_ff,
                                  T_p, t, act, S.TP_BF16)
         torch.cuda.synchronize()
-        _assert_within_one_step(h2, h_ref, f"H({t}) from registers")
+        _assert_within_one_step(h2, h_ref, f"H({t}) of the training forward")
         assert np.array_equal(host64(u2), u_ref), "saved U is not the pre-activation"
         if v2 is not None:
             assert np.array_equal(host64(v2), v_ref), "saved V is not the gate"
