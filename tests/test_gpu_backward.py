@@ -253,12 +253,12 @@ def _sampled_backward(w: I.Workload, t: int, n_rows: int, n_cols: int):
 
 @pytest.mark.slow
 def test_backward_llama3_8b_shape_sampled():
-    _sampled_backward(I.WORKLOADS[3], t=5, n_rows=256, n_cols=16)
+    _sampled_backward(I.WORKLOADS[3], t=5, n_rows=1024, n_cols=16)
 
 
 @pytest.mark.slow
 def test_backward_llama3_70b_shape_sampled():
-    _sampled_backward(I.WORKLOADS[4], t=3, n_rows=128, n_cols=8)
+    _sampled_backward(I.WORKLOADS[4], t=3, n_rows=1024, n_cols=8)
 
 
 # ----------------------------------------------------------------------------- out-projection backward
@@ -324,7 +324,7 @@ def test_outproj_backward_llama3_70b_shape_sampled():
                            S.TP_F32)
     dy64 = f64(dy, w.dtype)
     wr = f64(wo[t * k:(t + 1) * k], w.dtype)
-    rows = sample_rows(T, 256, 77)
+    rows = sample_rows(T, 1024, 77)
     e1 = nerr(host64(do[torch.as_tensor(rows, device="cuda:0")]), dy64[rows] @ wr.T)
     cols = np.unique(np.concatenate([[0, k - 1], np.random.default_rng(5).choice(k, 16, False)]))
     e2 = nerr(host64(dwo)[t * k + cols], f64(o[:, cols], w.dtype).T @ dy64)
