@@ -991,7 +991,7 @@ def measure_configs(steps: int, warmup: int):
     return res, keep
 
 
-def cpu_check_configs(results: dict, kept: dict, rows_n: int = 64) -> None:
+def cpu_check_configs(results: dict, kept: dict, rows_n: int = 1024) -> None:
     """The oracle on a seeded sample of token rows of each smaller workload, against the
     GPU's reduced output y (normwise max error, and the oracle's time for the sample)."""
     import numpy as np
