@@ -6,6 +6,7 @@ CPU only) and checks that at least one pin test then fails.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -205,3 +206,15 @@ def test_planted_interleaved_bubble_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(A, "bubble_interleaved_step", _interleaved_step_squared)
     with pytest.raises(AssertionError):
         pins.test_interleaved_bubble_forms_agree()
+
+
+def _ring_bytes_one_pass(n_gpus, payload_bytes):
+    """Planted mistake: only the reduce-scatter's (N-1)/N of the payload."""
+    return Fraction(n_gpus - 1, n_gpus) * payload_bytes
+
+
+def test_planted_ring_allreduce_bytes_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "ring_allreduce_bytes_per_gpu", _ring_bytes_one_pass)
+    for n in (2, 8):
+        with pytest.raises(AssertionError):
+            pins.test_ring_allreduce_bytes_by_simulation(n)

@@ -366,3 +366,30 @@ def test_reduce_scatter_rows_gather_to_the_all_reduce(T_p):
     if T_p > 1:
         with pytest.raises(ValueError):
             O.reduce_scatter_rows([p[:T - 1] for p in parts], T_p, 0)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_ring_allreduce_bytes_by_simulation(n):
+    """S17 "Mechanics": a ring all-reduce over N GPUs moves 2(N-1)/N times the payload per
+    GPU.  Pinned by running one: a reduce-scatter (at step s GPU g passes its partial of
+    chunk g-s to GPU g+1, which adds it) then an all-gather (GPU g passes its finished chunk
+    g+1-s on), on integer vectors.  Every GPU must end with the exact sum, and each must
+    have sent exactly the bytes the formula gives."""
+    rng = np.random.default_rng(100 + n)
+    data = [rng.integers(-9, 10, 6 * n).astype(np.int64) for _ in range(n)]
+    chunks = [np.array_split(v.copy(), n) for v in data]
+    sent = [0] * n
+    for s in range(n - 1):     # reduce-scatter; messages of one step leave together
+        msgs = [(g, (g - s) % n, chunks[g][(g - s) % n].copy()) for g in range(n)]
+        for g, c, m in msgs:
+            chunks[(g + 1) % n][c] = chunks[(g + 1) % n][c] + m
+            sent[g] += m.nbytes
+    for s in range(n - 1):     # all-gather of the finished chunks
+        msgs = [(g, (g + 1 - s) % n, chunks[g][(g + 1 - s) % n].copy()) for g in range(n)]
+        for g, c, m in msgs:
+            chunks[(g + 1) % n][c] = m
+            sent[g] += m.nbytes
+    total = np.sum(data, axis=0)
+    for g in range(n):
+        assert np.array_equal(np.concatenate(chunks[g]), total)
+        assert sent[g] == analytic.ring_allreduce_bytes_per_gpu(n, data[0].nbytes)
