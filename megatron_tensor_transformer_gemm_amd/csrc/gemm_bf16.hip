@@ -181,9 +181,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   constexpr int A_BYTES = BM * AROWB;
   constexpr int SUB_BYTES = BK * BNS * 2;
   constexpr int STAGE = A_BYTES + NSUB * SUB_BYTES;
-  constexpr int A_LD = A_BYTES / 1024 / NW;   // 1 KiB buffer->LDS copies per wave per stage
-  constexpr int B_LD = NSUB * SUB_BYTES / 1024 / NW;
-  constexpr int LPS = A_LD + B_LD;            // copies per wave per stage
+  // Waves that issue the copies: with 8 waves only waves 0-3, one per SIMD (waves go to
+  // the SIMDs round-robin), so that a wave held at copy issue, which also slows the other
+  // wave of its SIMD, has a partner with no copies of its own to be held on (70B backward
+  // 39.7 -> 39.4 ms per step, training forward 2,327 -> 2,297 us per rank, GPT block 9.18
+  // -> 9.01 ms; three alternations on one box).
+  constexpr int CW = NW == 8 ? NW / 2 : NW;
+  constexpr int A_LD = A_BYTES / 1024 / CW;   // 1 KiB buffer->LDS copies per copying wave per stage
+  constexpr int B_LD = NSUB * SUB_BYTES / 1024 / CW;
+  constexpr int LPS = A_LD + B_LD;            // copies per copying wave per stage
   constexpr int QSUB = SUB_BYTES / 1024;      // copies per sub-tile
   constexpr int CPR = BNS / 8;                // 16-byte chunks per B row ([BK][BN] tile)
   constexpr int PITCH = BNS * 2;              // bytes per B row ([BK][BN] tile)
@@ -204,8 +210,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     if constexpr ((CPR & (CPR - 1)) == 0) return swz_b(r) & (CPR - 1);
     else return (r & 3) << 1;
   };
-  static_assert(A_BYTES % (1024 * NW) == 0 && (NSUB * SUB_BYTES) % (1024 * NW) == 0,
-                "copies split evenly over the waves");
+  static_assert(A_BYTES % (1024 * CW) == 0 && (NSUB * SUB_BYTES) % (1024 * CW) == 0,
+                "copies split evenly over the copying waves");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(BM % (32 * WMG) == 0, "whole 32-row blocks per wave");
   static_assert(KSUB % 2 == 0 && (ACPR == 4 || ACPR == 8), "BK must be 32 or 64");
@@ -231,6 +237,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WNG, wn = wave % WNG;
+  const bool copier = CW == NW || wave < CW;
+  const int cwave = CW == NW ? wave : wave % CW;   // the copies a copying wave issues
   int tm, tn;
   // split-K: workgroups [s * tiles, (s + 1) * tiles) take k range s (forward layout only)
   int split = 0, bid = blockIdx.x;
@@ -290,7 +298,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   int a_kc[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int q = wave * A_LD + i;
+    const int q = cwave * A_LD + i;
     if constexpr (A_KC) {
       const int row = q * ARPI + lane / ACPR;
       const int c = (lane % ACPR) ^ swz_a<ACPR>(row);
@@ -308,7 +316,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   int b_kr[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int q = wave * B_LD + i;
+    const int q = cwave * B_LD + i;
     const int pos = (q % QSUB) * 64 + lane;
     if constexpr (B_KC) {
       const int row = pos / ACPR;
@@ -323,7 +331,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     }
   }
   // B sub-tile a wave's copies land in is the same for all of its copies.
-  const bool b_second = (wave * B_LD) / QSUB != 0;
+  const bool b_second = (cwave * B_LD) / QSUB != 0;
 
   // Copies [first, first + count) of stage kt's LPS per wave (A copies first, then B).
   auto issue_range = [&](int kt, LDS_AS unsigned char* base, int first, int count) {
@@ -356,14 +364,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     for (int i = 0; i < A_LD; ++i) {
       if (i < first || i >= first + count) continue;
       const uint32_t v = (full || k0 + a_kc[i] < Kc) ? a_voff[i] : kOOB;
-      copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (wave * A_LD + i) * 1024));
+      copy16_to_lds(da, v, __builtin_amdgcn_readfirstlane(lds + (cwave * A_LD + i) * 1024));
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       if (A_LD + i < first || A_LD + i >= first + count) continue;
       const uint32_t v = (full || k0 + b_kr[i] < Kc) ? b_voff[i] : kOOB;
       copy16_to_lds(db, v,
-                    __builtin_amdgcn_readfirstlane(lds + A_BYTES + (wave * B_LD + i) * 1024));
+                    __builtin_amdgcn_readfirstlane(lds + A_BYTES + (cwave * B_LD + i) * 1024));
     }
   };
   auto issue = [&](int kt, LDS_AS unsigned char* base) { issue_range(kt, base, 0, LPS); };
@@ -533,7 +541,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
 
   // prologue: NST stages in flight, then stage 0's first fragments
 #pragma unroll
-  for (int p = 0; p < NST; ++p) issue(p, buf(p));
+  for (int p = 0; p < NST; ++p)
+    if (copier) issue(p, buf(p));
   sync_copies<(NST - 1) * LPS>();
   load_frags(buf(0), 0, af[0], bfr[0]);
 
@@ -571,7 +580,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
 #pragma unroll
       for (int j = 0; j < NITEM; ++j) {
         if (j * NMFMA / NITEM != i) continue;
-        if (j < LPS) issue_range(kt + NST, cur, j, 1);
+        if (j < LPS) {
+          if (copier) issue_range(kt + NST, cur, j, 1);
+        }
         else read_group(nxt, 0, af[0], bfr[0], j - LPS);
       }
       __builtin_amdgcn_sched_barrier(0);
