@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   // B sub-tile a wave's copies land in is the same for all of its copies.
   const bool b_second = (cwave * B_LD) / QSUB != 0;
 
-  // Copies [first, first + count) of stage kt's LPS per wave (A copies first, then B).
+  // Copies [first, first + count) of stage kt's LPS per copying wave (A copies first, then B).
   auto issue_range = [&](int kt, LDS_AS unsigned char* base, int first, int count) {
     int k0 = kt * BK;
     int Kc = Kv;
@@ -559,7 +559,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     __builtin_amdgcn_sched_barrier(0);
     // Stage kt+1 is complete for every wave; stage kt's buffer is free for stage kt+NST.
     // Past the end the copies are all out of range (zero fill, no memory traffic), so
-    // every stage issues the same number of copies and the loop has no branches.
+    // every stage issues the same number of copies and the loop has no data-dependent
+    // branches (only the wave-uniform one that skips copies on the non-copying waves).
     sync_copies<(NST - 2) * LPS>();
     // The last substep: its MFMAs with stage kt+NST's copies and then the next stage's
     // first fragment reads spread between them, items j = 0 .. LPS+NFR-1 (copies first)
@@ -582,8 +583,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
         if (j * NMFMA / NITEM != i) continue;
         if (j < LPS) {
           if (copier) issue_range(kt + NST, cur, j, 1);
+        } else {
+          read_group(nxt, 0, af[0], bfr[0], j - LPS);
         }
-        else read_group(nxt, 0, af[0], bfr[0], j - LPS);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
