@@ -331,6 +331,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
     }
   }
   // B sub-tile a wave's copies land in is the same for all of its copies.
+  static_assert(QSUB % B_LD == 0, "a copying wave's B copies stay within one sub-tile");
   const bool b_second = (cwave * B_LD) / QSUB != 0;
 
   // Copies [first, first + count) of stage kt's LPS per copying wave (A copies first, then B).
@@ -993,6 +994,7 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) b_kr[i] = (((cwave * B_LD + i) % QSUB) * 64 + lane) / CPR;
+  static_assert(QSUB % B_LD == 0, "a copying wave's B copies stay within one sub-tile");
   const bool b_second = (cwave * B_LD) / QSUB != 0;
   uint32_t a_voff[A_LD], b_voff[B_LD];
   const __bf16* A = nullptr;
