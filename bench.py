@@ -72,6 +72,20 @@ def load_traffic(kernel: str, workload: str, path: str | None = None):
     return ent.get("bytes_per_launch")
 
 
+def column_gemm_traffic_bounds(T: int, d: int, n: int) -> tuple:
+    """Bytes per launch of the gated column GEMM (bf16 X [T, d] times the W1 and W3 column
+    blocks [d, n], H [T, n] written): the compulsory bytes, and the bytes the persistent
+    256 x 256 tiling implies.  Each XCD's 32 concurrent tiles form a 4 x 8 block whose
+    k-sweep streams 4 A and 8 B panels (256 x d each) through the XCD's L2, once per sweep
+    of 256 tiles; H is written once.  (The model is for products of whole sweeps, such as
+    the 70B shard's 1,792 tiles.)"""
+    compulsory = 2 * (T * d + 2 * d * n + T * n)
+    tiles = -(-T // 256) * -(-(2 * n) // 256)
+    sweeps = -(-tiles // 256)
+    model = sweeps * 8 * (4 + 8) * (256 * d * 2) + 2 * T * n
+    return compulsory, model
+
+
 def host_cpu_info() -> dict:
     """The host's CPU model, its physical cores and the logical CPUs this process may use
     (from /proc/cpuinfo and the affinity mask)."""
@@ -352,6 +366,9 @@ def main() -> int:
                 "traffic": load_traffic("column_gemm_swiglu", w.name),
                 "kernel": "column-parallel GEMM + SwiGLU epilogue (per rank)",
                 "flops_per_launch": fl_col}
+    # what `traffic` compares with: the bytes the kernel must move, and what its tiling
+    # streams from beyond L2 at best (the rest is workgroups drifting apart)
+    roofline["traffic_compulsory"], roofline["traffic_tiling_model"] = column_gemm_traffic_bounds(T, d, n)
     if sclk:
         # the same kernel against the MFMA rate at the clock the power manager set
         roofline["frac_at_measured_sclk"] = round(

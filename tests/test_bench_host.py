@@ -93,3 +93,11 @@ def test_parity_failures_name_every_failed_check():
 def test_percentiles_nearest_rank():
     st = bench.percentiles([float(v) for v in range(100, 0, -1)])
     assert (st["median"], st["p10"], st["p90"], st["calls"]) == (51.0, 11.0, 90.0, 100)
+
+
+def test_column_gemm_traffic_bounds_of_the_70b_shard():
+    # X 16384 x 8192, W1 and W3 blocks 8192 x 3584, H 16384 x 3584, all bf16
+    compulsory, model = bench.column_gemm_traffic_bounds(16384, 8192, 3584)
+    assert compulsory == 2 * (16384 * 8192 + 2 * 8192 * 3584 + 16384 * 3584) == 503_316_480
+    # 64 x 28 = 1,792 tiles: 7 sweeps x 8 XCDs x 12 panels of 256 x 8192 bf16, plus H
+    assert model == 7 * 8 * 12 * (256 * 8192 * 2) + 2 * 16384 * 3584 == 2_936_012_800
