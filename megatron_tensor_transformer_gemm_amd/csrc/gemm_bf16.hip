@@ -921,9 +921,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
 // ---- Forward products of more than one wave of 256 x 256 tiles: one workgroup per CU
 // takes tiles gridDim.x apart, and the copy pipeline runs on across tile boundaries.  The
 // second-to-last stage of a tile copies k-tile 0 of the workgroup's next tile (instead of
-// the zero fill that pads a lone tile's loop); the last stage copies nothing, so that
-// k-tile 0 arrives while the last stages multiply and the epilogue runs, and is waited
-// for after it (with k-tile 1 issued then).  The epilogue therefore may not use the stage
+// the zero fill that pads a lone tile's loop); the last stage copies nothing (beyond the
+// deferred part of that k-tile, in the plain products), so that k-tile 0 arrives while
+// the last stages multiply and the epilogue runs, and is waited for after it (with
+// k-tile 1 issued then).  The epilogue therefore may not use the stage
 // buffers: each wave rounds its 128-row block 32 rows at a time into a 4 KiB region of
 // its own (32 KiB beside the two 64 KiB stages: the whole 160 KiB of LDS) and stores
 // whole row segments from there, with no workgroup barrier.
@@ -1113,6 +1114,18 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
       bfr[0][nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
+  // fragment group j (A groups, then B groups) of substep s into register set st
+  auto read_grp = [&](const LDS_AS unsigned char* As, int s, int st, int j) {
+    if (j < MB) {
+      af[st][j] = *(const LDS_AS bf16x8*)(As + a_rd[s] + j * 32 * AROWB);
+    } else {
+      const int nb = j - MB;
+      const LDS_AS unsigned char* p = As + A_BYTES + b_rd[nb] + 16 * s * PITCH;
+      bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p));
+      bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)(p + 4 * PITCH));
+      bfr[st][nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
   auto mfmas = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[NB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -1143,14 +1156,56 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
 
   // One stage of the tile (all but the last); at stage nk - NST the copies move on to
   // the next tile.
-  auto stage = [&](int kt, int u) {
-    LDS_AS unsigned char* cur = buf(u);
-    LDS_AS unsigned char* nxt = buf(u + 1 == NST ? 0 : u + 1);
+  // Copies deferred by one substep.  The buffer a stage's barrier frees is not read again
+  // until after the next stage's barrier, so the plain products (row GEMM, out-projection)
+  // issue the last DEFC of each copying wave's copies for it in the next stage's first
+  // substep instead of the stage tail: the copy path (16-18 cycles per 1 KiB copy per CU)
+  // then works over twice the window.  70B row GEMM 750 -> 735 us, out-projection 245 ->
+  // 241.5 us (three alternations, one box).  The gated column GEMM, whose A panels come
+  // from beyond L2 more often, keeps every copy in the tail: the later copies have less
+  // time to land before the next barrier, and deferring 2 or 4 of 8 there was slower.
+  constexpr int NFR = MB + NB;
+  constexpr int DEFC = DUAL ? 0 : LPS / 2;
+  // Substep 0 of a stage: its MFMAs, the fragment reads of substep 1 and the deferred
+  // copies of k-tile kd into nb_buf (`copies`: false where the previous stage left none).
+  auto sub0 = [&](const LDS_AS unsigned char* cur, LDS_AS unsigned char* nb_buf, int kd, bool copies) {
+    constexpr int NIT = NFR + DEFC;
 #pragma unroll
-    for (int s = 0; s + 1 < KSUB; ++s) {
+    for (int i = 0; i < NMFMA; ++i) {
+      const int mb = i / NB, nb = i % NB;
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[0][nb], af[0][mb], acc[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        if (j * NMFMA / NIT != i) continue;
+        if (j < NFR) {
+          read_grp(cur, 1, 1, j);
+        } else {
+          if (copier && copies) issue_range(kd, nb_buf, LPS - DEFC + (j - NFR), 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the substeps from `first` on whose reads are of the same stage
+  auto substeps = [&](const LDS_AS unsigned char* cur, int first) {
+#pragma unroll
+    for (int s = first; s + 1 < KSUB; ++s) {
       load_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
       mfmas(af[s & 1], bfr[s & 1]);
       interleave();
+    }
+  };
+  auto stage = [&](int kt, int u) {
+    LDS_AS unsigned char* cur = buf(u);
+    LDS_AS unsigned char* nxt = buf(u + 1 == NST ? 0 : u + 1);
+    if constexpr (DEFC > 0) {
+      // k-tile kt+1's deferred copies (none at a tile's first stage: the transition
+      // copies k-tile 1 whole)
+      sub0(cur, nxt, kt + 1, kt != 0);
+      substeps(cur, 1);
+    } else {
+      substeps(cur, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // k-tile kt+1 (of this tile or the next) is complete for every wave; this stage's
@@ -1168,8 +1223,7 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
     }
     const int kc = kt + NST < nk ? kt + NST : kt + NST - nk;
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int NFR = MB + NB;
-    constexpr int NITEM = LPS + NFR;
+    constexpr int NITEM = LPS - DEFC + NFR;
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int mb = i / NB, nb = i % NB;
@@ -1178,10 +1232,10 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
 #pragma unroll
       for (int j = 0; j < NITEM; ++j) {
         if (j * NMFMA / NITEM != i) continue;
-        if (j < LPS) {
+        if (j < LPS - DEFC) {
           if (copier) issue_range(kc, cur, j, 1);
         } else {
-          read_group(nxt, j - LPS);
+          read_group(nxt, j - (LPS - DEFC));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1221,15 +1275,16 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
       for (int u = 0; u < NST; ++u) stage(kt0 + u, u);
     }
     stage(nk - 2, 0);   // copies k-tile 0 of the next tile
-    // The last stage: no copies and no reads of the next stage, so that the next tile's
-    // k-tile 0 (copied since stage nk - 2) is waited for only after the epilogue.
+    // The last stage: no copies (but the deferred part of the next tile's k-tile 0) and no
+    // reads of the next stage, so that the next tile's k-tile 0 (copied since stage
+    // nk - 2) is waited for only after the epilogue.
     {
       const LDS_AS unsigned char* cur = buf(1);
-#pragma unroll
-      for (int s = 0; s + 1 < KSUB; ++s) {
-        load_frags(cur, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-        mfmas(af[s & 1], bfr[s & 1]);
-        interleave();
+      if constexpr (DEFC > 0) {
+        sub0(cur, buf(0), 0, true);   // the next tile's k-tile 0, deferred part
+        substeps(cur, 1);
+      } else {
+        substeps(cur, 0);
       }
       mfmas(af[1], bfr[1]);
     }
