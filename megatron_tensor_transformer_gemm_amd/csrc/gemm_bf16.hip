@@ -548,15 +548,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   load_frags(buf(0), 0, af[0], bfr[0]);
 
   // One stage; `u` is the stage's buffer (kt mod NST), a constant after unrolling.
-  // Copies deferred by one substep (the backward's NT and TN products on 8 waves): the
-  // buffer a stage's barrier frees is not read again before the next stage's barrier, so
-  // each copying wave issues the last DEFC of its copies for it in the next stage's first
-  // substep, and the copy path works over twice the window.  70B backward, 8 ranks, three
-  // alternations on one box: 38.72-38.85 -> 38.49-38.53 ms per step.  The forward layout
-  // keeps every copy in the stage tail (its later copies landed too late: GPT block +2.8 %,
-  // training forward +1.3 %).
+  // Copies deferred by one substep (the backward's dX and weight-gradient products on 8
+  // waves): the buffer a stage's barrier frees is not read again before the next stage's
+  // barrier, so each copying wave issues the last DEFC of its copies for it in the next
+  // stage's first substep, and the copy path works over twice the window.  70B rank,
+  // kernel traces, two runs each: dW1|dW3 and dW2 (TN) 1,276 -> 1,233 us on average, dX
+  // (NT) 1,535 -> 1,520 us.  Not used for the dH product with the activation's derivative
+  // (128 x 256 tiles, three stages: 936 -> 1,013 us), nor for tiles with fewer than 8 MFMAs
+  // per substep to spread the extra items over (as those), nor in the forward layout (its
+  // later copies landed too late: GPT block +2.8 %, training forward +1.3 %).
   constexpr int NFR = MB + NB;
-  constexpr int DEFC = (NW == 8 && LAYOUT != kNN) ? LPS / 2 : 0;
+  constexpr int DEFC = (NW == 8 && LAYOUT != kNN && ACT == kActNone && MB * NB >= 8) ? LPS / 2 : 0;
   auto stage = [&](int kt, int u) {
     LDS_AS unsigned char* cur = buf(u);
     LDS_AS unsigned char* nxt = buf(u + 1 == NST ? 0 : u + 1);
