@@ -210,7 +210,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU: every tensor-parallel "
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU: every tensor-parallel "
                                    "rank's shard runs on that GPU and a local partial sum stands "
                                    "in for the all-reduce; --gpus above 1 is not supported",
                           "n_gpus": args.gpus}), flush=True)
