@@ -962,8 +962,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
 // second-to-last stage of a tile copies k-tile 0 of the workgroup's next tile (instead of
 // the zero fill that pads a lone tile's loop); the last stage copies nothing (beyond the
 // deferred part of that k-tile, in the plain products), so that k-tile 0 arrives while
-// the last stages multiply; k-tile 1 is issued before the epilogue, and k-tile 0 waited
-// for before the epilogue's first store.  The epilogue therefore may not use the stage
+// the last stages multiply; k-tile 1 is issued between the last stage's final MFMAs,
+// and k-tile 0 waited for before the epilogue's first store.  The epilogue therefore may not use the stage
 // buffers: each wave rounds its 128-row block 32 rows at a time into a 4 KiB region of
 // its own (32 KiB beside the two 64 KiB stages: the whole 160 KiB of LDS) and stores
 // whole row segments from there, with no workgroup barrier.
@@ -1314,9 +1314,10 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
       for (int u = 0; u < NST; ++u) stage(kt0 + u, u);
     }
     stage(nk - 2, 0);   // copies k-tile 0 of the next tile
-    // The last stage: no copies (but the deferred part of the next tile's k-tile 0) and no
-    // reads of the next stage, so that the next tile's k-tile 0 (copied since stage
-    // nk - 2) is waited for only after the epilogue.
+    // The last stage: no reads of the next stage and no wait for copies, so that the next
+    // tile's k-tile 0 (copied since stage nk - 2, and in the plain products partly in this
+    // stage's first substep) is waited for only in the epilogue; its last MFMAs carry the
+    // next tile's k-tile 1 copies.
     {
       const LDS_AS unsigned char* cur = buf(1);
       if constexpr (DEFC > 0) {
@@ -1325,19 +1326,31 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
       } else {
         substeps(cur, 0);
       }
-      mfmas(af[1], bfr[1]);
+      // Every wave has read buffer 1 once its last fragment reads are done: the next
+      // tile's k-tile 1 goes in during the last MFMAs, ahead of this tile's stores in the
+      // copy path.  (Against issuing it after the epilogue, which made the transition wait
+      // for the stores: out-projection 238.7 -> 234.4 us, row GEMM 732 -> 729 us; issuing
+      // it between the last MFMAs rather than after them: row GEMM 724.9 -> 720.5 us.
+      // Three alternations on one box each.)
+      __builtin_amdgcn_sched_barrier(0);
+      if (next_ok) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NMFMA; ++i) {
+        const int mb = i / NB, nb = i % NB;
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][nb], af[1][mb], acc[mb][nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < LPS; ++j) {
+          if (j * NMFMA / LPS != i) continue;
+          if (copier && next_ok) issue_range(1, buf(1), j, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // ---- epilogue: 32 rows at a time through this wave's own region; the next tile's
     // first stages are in flight meanwhile.  (The lane index goes through an empty asm so
     // that the epilogue's per-lane offsets are formed here rather than hoisted out of the
     // tile loop, where they would hold registers through every k-loop.)
-    if (next_ok) {
-      // every wave has read buffer 1: the next tile's k-tile 1 goes in now, ahead of this
-      // tile's stores in the copy path (70B out-projection 238.7 -> 234.4 us, row GEMM
-      // 732 -> 729 us, three alternations on one box)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (copier) issue_range(1, buf(1), 0, LPS);
-    }
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
