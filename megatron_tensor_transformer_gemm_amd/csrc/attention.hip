@@ -158,7 +158,7 @@ __global__ void __launch_bounds__(kWaves * 64) attention_kernel(AttnDesc a, int 
   // w + 4, on the same SIMD as wave w since waves go to the SIMDs round-robin).  A wave
   // held at copy issue also slows the other wave of its SIMD; here that other wave has no
   // copies of its own to be held on (causal core at 2,048 tokens, 6 heads: 24.6 -> 22.6 us,
-  // three alternations on one box).  Copy i covers rows c_row0 + i*RPC.  The V swizzle depends on the row mod
+  // three alternations on one GPU).  Copy i covers rows c_row0 + i*RPC.  The V swizzle depends on the row mod
   // 4 only, so its offsets step by a constant; the K swizzle needs one offset per copy.
   constexpr int RPC = 64 / CPR;          // rows per 1 KiB copy
   const int c_row0 = (qh * NC * 64 + lane) / CPR, c_slot = lane % CPR;

@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   // the SIMDs round-robin), so that a wave held at copy issue, which also slows the other
   // wave of its SIMD, has a partner with no copies of its own to be held on (70B backward
   // 39.7 -> 39.4 ms per step, training forward 2,327 -> 2,297 us per rank, GPT block 9.18
-  // -> 9.01 ms; three alternations on one box).
+  // -> 9.01 ms; three alternations on one GPU).
   constexpr int CW = NW == 8 ? NW / 2 : NW;
   constexpr int A_LD = A_BYTES / 1024 / CW;   // 1 KiB buffer->LDS copies per copying wave per stage
   constexpr int B_LD = NSUB * SUB_BYTES / 1024 / CW;
@@ -643,7 +643,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
   // The partials go through LDS as the bf16 outputs do: each wave stages half of its rows
   // at a time (its whole fp32 block does not fit in the stage buffers) and stores whole row
   // segments, 16 B per lane, instead of 32 B per row over 32 rows per instruction (GPT
-  // block, same box: 9.28 -> 9.21 ms per step).  Their bytes, not their pattern, are the
+  // block, same GPU: 9.28 -> 9.21 ms per step).  Their bytes, not their pattern, are the
   // cost: a timing-only variant that skips these stores ran the block 11 % faster.
   if (splitk) {
     float* P = g.part + (int64_t)split * g.pslice;
@@ -829,7 +829,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDesc g, int tile
       };
       // Products without an activation (row GEMM, out-projection, dX: partial sums that the
       // partial-sum kernel reads later, from HBM) are stored non-temporally (70B step, same
-      // box: out-projection 271 -> 266 us, the partial sum after the row GEMMs 439 -> 433
+      // GPU: out-projection 271 -> 266 us, the partial sum after the row GEMMs 439 -> 433
       // us).  H, which the row GEMM reads next, keeps ordinary stores (non-temporal ones
       // there measured level).
       auto store_out = [](const bf16x8& v, bf16x8* dst) {
@@ -1200,7 +1200,7 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
   // issue the last DEFC of each copying wave's copies for it in the next stage's first
   // substep instead of the stage tail: the copy path (16-18 cycles per 1 KiB copy per CU)
   // then works over twice the window.  70B row GEMM 750 -> 735 us, out-projection 245 ->
-  // 241.5 us (three alternations, one box).  The gated column GEMM, whose A panels come
+  // 241.5 us (three alternations, one GPU).  The gated column GEMM, whose A panels come
   // from beyond L2 more often, keeps every copy in the tail: the later copies have less
   // time to land before the next barrier, and deferring 2 or 4 of 8 there was slower.
   constexpr int NFR = MB + NB;
@@ -1331,7 +1331,7 @@ __global__ void __launch_bounds__(512) gemm_fwd_persistent_kernel(GemmDesc g, in
       // copy path.  (Against issuing it after the epilogue, which made the transition wait
       // for the stores: out-projection 238.7 -> 234.4 us, row GEMM 732 -> 729 us; issuing
       // it between the last MFMAs rather than after them: row GEMM 724.9 -> 720.5 us.
-      // Three alternations on one box each.)
+      // Three alternations on one GPU each.)
       __builtin_amdgcn_sched_barrier(0);
       if (next_ok) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
@@ -1607,7 +1607,7 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
       const int64_t last = big % 256;
       // 128x256 tiles leave LDS for a third 64-deep stage (3 x 48 KiB); measured on the 70B
       // dH product (1,792 tiles): 1,171 -> 1,089 us against two stages
-      // 8 waves, as the forward tiles (70B backward, same box: 43.3-44.0 -> 42.2 ms per step
+      // 8 waves, as the forward tiles (70B backward, same GPU: 43.3-44.0 -> 42.2 ms per step
       // together with the TN products below; either layout alone gained less)
       if (last != 0 && last <= 192) return launch_cfg<128, 256, 64, 3, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
       return launch_cfg<256, 256, 64, 2, DUAL, ACT, OUT_F32, LAYOUT, SAVE, 8>(g, s);
@@ -1668,7 +1668,7 @@ hipError_t launch_sized(const GemmDesc& g, hipStream_t s) {
   if (big >= 256) {
     // Forward 256 x 256 tiles: 8 waves (two per SIMD, 128 x 64 each) with two 64-deep
     // stages.  While one wave of a SIMD is held issuing a copy the other keeps the matrix
-    // pipe fed; measured alone (same operands repeated, same box) against 4 waves with four
+    // pipe fed; measured alone (same operands repeated, same GPU) against 4 waves with four
     // 32-deep stages: 70B column GEMM + SwiGLU 1,440 against 1,470 us, row GEMM 735-748
     // against 754 us, out-projection 257-261 against 273 us (two 64-deep stages).
     if constexpr (LAYOUT == kNN && !SAVE) {
