@@ -274,6 +274,33 @@ def test_partial_sum_integers_exact_and_in_place():
     assert np.array_equal(host64(y), ref)
 
 
+def test_partial_sum_past_one_grid_pass():
+    """An array longer than one pass of the partial sum's grid (2^28 vectors of 8, the largest
+    grid it launches): 2^31 + 13 bf16 elements over 2 slices, so one vector is summed on a
+    second pass and 5 elements by the scalar tail.  Small integer partials make every sum
+    exact in bf16: the sampled outputs (every pass and tail boundary, and 4,096 seeded
+    positions) equal the oracle's sum exactly, and no output is left unwritten."""
+    T_p, n = 2, (1 << 31) + 13
+    stride = n + 3                                  # a multiple of 8
+    log(f"[partial sum past one grid pass] T_p={T_p} n={n} stride={stride}")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(31)
+    P = torch.randint(-64, 65, (T_p, stride), dtype=torch.int16, device="cuda:0", generator=gen)
+    P = P.to(torch.bfloat16)
+    y = torch.full((n,), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    S.tp_partial_sum(P, stride, T_p, None, y, n, S.TP_BF16, S.TP_BF16)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(y).any())
+    edge = 8 << 28                                  # first element of the second pass
+    idx = np.concatenate([np.arange(0, 16), np.arange(edge - 16, n),
+                          np.random.default_rng(31).integers(0, n, 4096)])
+    it = torch.from_numpy(idx).cuda()
+    parts = [host64(P[t].index_select(0, it)) for t in range(T_p)]
+    assert np.array_equal(host64(y.index_select(0, it)), O.partial_sum(parts))
+    del P, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T_p,pd,od", [(8, S.TP_BF16, S.TP_BF16), (4, S.TP_F32, S.TP_BF16),
                                         (2, S.TP_BF16, S.TP_F32)])
 def test_reduce_scatter_rows_are_the_sum_rows(T_p, pd, od):
